@@ -1,0 +1,58 @@
+"""Algorithmic work of one unmerged multi-LoRA call: bytes and FLOPs.
+
+These counts define what a launch *must* move and compute; they are what the
+benchmark divides by measured time.  They restate the cost model of
+"Serving several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
+alongside" (the ``lora_costs`` function and its printed FLUX table), which
+counts 2 N (d r + r d) extra FLOPs per adapted layer and d r 2 elements per
+LoRA, generalised to A: r x d_in, B: d_out x r.  The page's table is pinned in
+tests/golden/lora_costs_flux.txt.
+"""
+from __future__ import annotations
+
+from typing import Iterable
+
+
+def lora_flops(slot_tokens: int, r: int, d_in: int, d_out: int) -> int:
+    """FLOPs of the unmerged delta: 2 multiply-add FLOPs per MAC, r*d_in MACs for
+    the shrink and d_out*r for the expand, per (token, applied adapter)."""
+    return 2 * slot_tokens * (d_in * r + r * d_out)
+
+
+def adapter_bytes(r: int, d_in: int, d_out: int, elem: int) -> int:
+    """Bytes of one adapter: A (r x d_in) plus B (d_out x r)."""
+    return r * (d_in + d_out) * elem
+
+
+def call_bytes(touched_tokens: int, distinct_adapters: int, r: int, d_in: int, d_out: int, elem: int) -> int:
+    """Algorithmic HBM bytes of one fused call: every touched row of x read once,
+    every touched row of y read and written once, every adapter used read once."""
+    return touched_tokens * (d_in + 2 * d_out) * elem + distinct_adapters * adapter_bytes(r, d_in, d_out, elem)
+
+
+def batch_work(seg_bounds: Iterable, idx, n_adapters: int):
+    """(touched tokens, slot-tokens, distinct adapters) of a batch.
+    seg_bounds: [(start, end)] per request; idx: [S][K] with -1 = empty."""
+    touched = slot_tokens = 0
+    used = set()
+    for s, (lo, hi) in enumerate(seg_bounds):
+        L = max(0, hi - lo)
+        valid = [int(i) for i in idx[s] if 0 <= int(i) < n_adapters]
+        if L and valid:
+            touched += L
+            slot_tokens += L * len(valid)
+            used.update(valid)
+    return touched, slot_tokens, len(used)
+
+
+def lora_costs(d_model: int, layers: int, adapted_per_layer: int, rank: int, n_tokens: int,
+               hbm_gbps: float = 3350.0, dtype: int = 2):
+    """The page's cost model for a square d x d model: (extra compute relative to the
+    adapted layers, merge-or-unmerge time in ms, size of the LoRA in MiB)."""
+    n_layers = adapted_per_layer * layers
+    base = 2 * n_tokens * d_model * d_model * n_layers
+    extra = lora_flops(n_tokens, rank, d_model, d_model) * n_layers
+    weight_bytes = d_model * d_model * dtype * n_layers
+    merge_ms = 2 * weight_bytes / (hbm_gbps * 1e9) * 1e3
+    lora_mib = adapter_bytes(rank, d_model, d_model, dtype) * n_layers / 2 ** 20
+    return extra / base, merge_ms, lora_mib
