@@ -1,0 +1,185 @@
+/*
+ * lora.h -- C ABI of the MI355X (gfx950) unmerged multi-LoRA library.
+ *
+ * What the library computes.  "Serving several LoRAs, ControlNet and
+ * IP-Adapter", section "LoRA: merged or alongside": a LoRA adds the low-rank
+ * increment W' = W + BA with A of shape r x d and B of shape d x r, and the
+ * unmerged form adds x A^T B^T to the base output x W^T in every adapted
+ * layer.  Here A is r x d_in and B is d_out x r.  The same page, self-test
+ * answer on mixing LoRAs and the "Exercises" answer on four requests: every
+ * request carries its own LoRA index; the low-rank products are grouped by
+ * LoRA index, one kernel handles every group, and the results are added back
+ * into the base output in the original row order.  "Punica: Multi-Tenant LoRA
+ * Serving" (contribution 1) names the same idea segmented gather
+ * matrix-vector (SGMV) kernels for heterogeneous LoRA batches.  Stacked LoRAs
+ * are extra alongside computations that are summed (comparison table,
+ * "Stacking several LoRAs"); a per-slot scale is the swappable scalar of the
+ * timestep-varying LoRA weight (same section, the paragraph on diffusion).
+ *
+ * For each request s, each row t of that request, and each slot k whose index
+ * i = idx[s][k] is valid:
+ *
+ *     y[t][:] += scale[s][k] * (x[t][:] . A_i^T) . B_i^T
+ *
+ * accumulated in fp32 and rounded once (round-to-nearest-even) to y's type.
+ * Rows whose request has no valid slot, and rows covered by no request, are
+ * never written (their bits are left exactly as they were).
+ *
+ * Memory and ownership.  Every pointer in a struct or argument below is a
+ * DEVICE pointer unless its comment says "host".  All buffers are allocated
+ * and owned by the caller; the library allocates and frees nothing, keeps no
+ * global state and is re-entrant.  Every compute call is asynchronous on the
+ * given stream and never synchronizes, except lora_read_device_errors.
+ * x and y must not overlap; v must overlap neither x nor y.
+ *
+ * Errors.  Problems visible on the host (NULL pointers, non-positive sizes,
+ * unsupported rank or slot count, ld < d, a workspace that is too small,
+ * overlapping x/y) return a status and launch nothing.  Adapter indices and
+ * segment offsets live on the device and cannot be checked there: an index
+ * below -1 or >= n_adapters is skipped as if it were -1, and decreasing or
+ * out-of-range offsets are clamped into non-overlapping segments (segment s
+ * becomes [max(seg_off[0..s]), max(seg_off[0..s+1])) clipped to [0, T]); both
+ * are counted in a device error word read by lora_read_device_errors.
+ */
+#ifndef RANK_SGMV_BGMV_LORA_H
+#define RANK_SGMV_BGMV_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LORA_OK = 0,
+  LORA_EINVAL = -1,       /* NULL pointer, overlapping buffers, bad enum */
+  LORA_ESHAPE = -2,       /* non-positive size, ld < d, bad counts */
+  LORA_EWORKSPACE = -3,   /* workspace missing or smaller than lora_workspace_size */
+  LORA_EUNSUPPORTED = -4, /* rank, slot count or size beyond the limits below */
+  LORA_EHIP = -5          /* a HIP runtime call (launch) failed */
+} lora_status;
+
+/* x, y, A and B share one element type.  The intermediate of lora_shrink /
+ * lora_expand is always float32. */
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+#define LORA_MAX_RANK 256        /* 1 <= rank <= 256 */
+#define LORA_MAX_SLOTS 8         /* 1 <= max_slots <= 8 */
+#define LORA_MAX_SLOT_RANK 1024  /* max_slots * rank <= 1024 */
+
+/* One adapted linear layer's resident, stacked adapter pool ("Serving several
+ * LoRAs ...", section "Placement": every LoRA stays resident).
+ *   A: [n_adapters][rank][d_in]   row-major, dtype
+ *   B: [n_adapters][d_out][rank]  row-major, dtype                       */
+typedef struct {
+  const void *A;
+  const void *B;
+  int32_t n_adapters;
+  int32_t rank;
+  int32_t d_in;
+  int32_t d_out;
+  lora_dtype dtype;
+} lora_pool;
+
+/* The batch: which adapters apply to which rows.
+ *   n_tokens   T, rows of x and y.
+ *   n_segments S, number of requests; ignored when seg_off is NULL.
+ *   seg_off    [S+1] int32, request s owns rows [seg_off[s], seg_off[s+1]);
+ *              non-decreasing, 0 <= seg_off[0], seg_off[S] <= T.  Rows outside
+ *              [seg_off[0], seg_off[S]) belong to no request.  NULL selects
+ *              per-token mode: S = T and request s is row s (decode / BGMV).
+ *   idx        [S][max_slots] int32 adapter indices; -1 = empty slot.
+ *   max_slots  K, slots per request (stacked adapters are summed).
+ *   scale      [S][max_slots] float32 per-slot scale, or NULL for 1.0.     */
+typedef struct {
+  int32_t n_tokens;
+  int32_t n_segments;
+  const int32_t *seg_off;
+  const int32_t *idx;
+  int32_t max_slots;
+  const float *scale;
+} lora_batch;
+
+/* One problem of a lora_apply_multi launch: a pool and its activations.  The
+ * array of these lives in DEVICE memory; all problems share the shape given
+ * by the `shape` argument of lora_apply_multi.                           */
+typedef struct {
+  const void *A;   /* [n][rank][d_in]  */
+  const void *B;   /* [n][d_out][rank] */
+  const void *x;   /* [T][ldx] */
+  void *y;         /* [T][ldy], updated in place */
+  int64_t ldx;
+  int64_t ldy;
+} lora_problem;
+
+/* Bytes of device workspace (the plan) for a batch and pool size.  The plan
+ * holds the grouping of requests by adapter (stable across layers: build it
+ * once per batch and reuse it for every adapted layer).  Returns 0 when the
+ * batch description itself is invalid. */
+size_t lora_workspace_size(const lora_batch *batch, int32_t n_adapters);
+
+/* Build the plan for `batch` into `ws` on `stream`: sort requests by adapter
+ * (the grouping of the "Exercises" answer), split groups into row tiles, and
+ * record the device error word.  The batch arrays must stay unchanged until
+ * every call that uses the plan has run. */
+lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Fused apply: y += sum_k scale * (x A_i^T) B_i^T for every touched row.
+ * Builds the plan into ws, then runs the fused kernel.
+ *   x: [T][ldx] dtype, ldx >= d_in;  y: [T][ldy] dtype, ldy >= d_out.    */
+lora_status lora_apply(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
+                       int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Shrink half: v[t][k*rank + j] = scale[s][k] * sum_c x[t][c] A_i[j][c] for
+ * every touched row t and slot k (zeros for a -1 slot of a touched row).
+ * v: [T][ldv] float32, ldv >= max_slots*rank.  Rows that are not touched are
+ * not written. */
+lora_status lora_shrink(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, float *v,
+                        int64_t ldv, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expand half: y[t][o] += sum_{k valid} sum_j v[t][k*rank + j] B_i[o][j] for
+ * every touched row (the scale is not applied again: lora_shrink folded it
+ * in, so lora_expand(lora_shrink(x)) computes what lora_apply does). */
+lora_status lora_expand(const lora_pool *pool, const lora_batch *batch, const float *v, int64_t ldv, void *y,
+                        int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same three operations on a plan built earlier by lora_plan_build for
+ * this batch (plan_bytes as returned by lora_workspace_size). */
+lora_status lora_apply_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                               const void *x, int64_t ldx, void *y, int64_t ldy, hipStream_t stream);
+lora_status lora_shrink_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                                const void *x, int64_t ldx, float *v, int64_t ldv, hipStream_t stream);
+lora_status lora_expand_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                                const float *v, int64_t ldv, void *y, int64_t ldy, hipStream_t stream);
+
+/* Many adapted layers of one shape in ONE launch, sharing one plan: for each
+ * of the n_problems entries of `problems` (a DEVICE array), the fused apply
+ * with that problem's pool, x and y.  `shape` gives rank, d_in, d_out,
+ * n_adapters and dtype (its A and B are ignored).  The library cannot check
+ * the pointers inside the device array; they must satisfy the alignment and
+ * ld rules of lora_apply for this shape (16-byte aligned, ld a multiple of 8
+ * elements for bf16 or 4 for fp32, for the vectorised path) or the launch
+ * uses the scalar path only when `problems_aligned` is 0. */
+lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                             int32_t n_problems, const lora_problem *problems, int32_t problems_aligned,
+                             hipStream_t stream);
+
+/* Synchronizes `stream` and stores in *count the number of invalid adapter
+ * indices and segment-offset violations the last plan build met. */
+lora_status lora_read_device_errors(const void *plan, size_t plan_bytes, int32_t *count, hipStream_t stream);
+
+/* Static, human-readable text for a status. */
+const char *lora_status_string(lora_status status);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t lora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANK_SGMV_BGMV_LORA_H */

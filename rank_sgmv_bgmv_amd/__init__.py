@@ -1,1 +1,246 @@
-"""Unmerged multi-LoRA (SGMV / BGMV) for AMD MI355X (gfx950)."""
+"""Unmerged multi-LoRA (SGMV / BGMV) for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C-ABI library ``_build/liblora_hip.so``
+(declared in ``include/lora.h``).  Every function here only marshals torch
+tensors into pointers, sizes and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback: if
+the library has not been built, calls raise ``LoraError``.
+
+Functions carry the C names:
+  lora_workspace_size, lora_plan_build, lora_apply, lora_shrink, lora_expand,
+  lora_apply_planned, lora_shrink_planned, lora_expand_planned,
+  lora_apply_multi, lora_read_device_errors, lora_status_string.
+
+Tensors: A [n][r][d_in] and B [n][d_out][r] contiguous (float32 or bfloat16);
+x [T][ldx], y [T][ldy] with unit column stride (ld = stride(0)); idx int32
+[S][K]; seg_off int32 [S+1] or None (one token per request); scale float32
+[S][K] or None; v float32 [T][ldv]; workspace/plan a uint8 device tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+from . import accounting  # noqa: F401  (pure Python byte/FLOP accounting)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "liblora_hip.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+STATUS = {0: "LORA_OK", -1: "LORA_EINVAL", -2: "LORA_ESHAPE", -3: "LORA_EWORKSPACE", -4: "LORA_EUNSUPPORTED",
+          -5: "LORA_EHIP"}
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = STATUS.get(status, str(status))
+        super().__init__(f"{what}: {msg}" if what else msg)
+
+
+class lora_pool(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("n_adapters", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("dtype", ctypes.c_int)]
+
+
+class lora_batch(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("n_segments", ctypes.c_int32), ("seg_off", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("max_slots", ctypes.c_int32), ("scale", ctypes.c_void_p)]
+
+
+class lora_problem(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("ldx", ctypes.c_int64), ("ldy", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises LoraError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LoraError(-5, f"HIP library not built ({LIB_PATH}); run python -m rank_sgmv_bgmv_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        pp, pb = ctypes.POINTER(lora_pool), ctypes.POINTER(lora_batch)
+        sig = {
+            "lora_workspace_size": (SZ, [pb, I32]),
+            "lora_plan_build": (ctypes.c_int, [pb, I32, P, SZ, P]),
+            "lora_apply": (ctypes.c_int, [pp, pb, P, I64, P, I64, P, SZ, P]),
+            "lora_shrink": (ctypes.c_int, [pp, pb, P, I64, P, I64, P, SZ, P]),
+            "lora_expand": (ctypes.c_int, [pp, pb, P, I64, P, I64, P, SZ, P]),
+            "lora_apply_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
+            "lora_shrink_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
+            "lora_expand_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
+            "lora_apply_multi": (ctypes.c_int, [pp, pb, P, SZ, I32, P, I32, P]),
+            "lora_read_device_errors": (ctypes.c_int, [P, SZ, ctypes.POINTER(I32), P]),
+            "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "lora_abi_version": (I32, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------- marshalling --
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return LORA_F32
+    if t.dtype == torch.bfloat16:
+        return LORA_BF16
+    raise LoraError(-1, f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise LoraError(st, what)
+
+
+class Pool:
+    """A resident adapter pool: A [n][r][d_in], B [n][d_out][r]."""
+
+    def __init__(self, A, B):
+        if A.dim() != 3 or B.dim() != 3 or not A.is_contiguous() or not B.is_contiguous():
+            raise LoraError(-2, "A and B must be contiguous 3-D tensors")
+        n, r, d_in = A.shape
+        if B.shape[0] != n or B.shape[2] != r or B.dtype != A.dtype:
+            raise LoraError(-2, "B must be [n][d_out][r] with A's dtype")
+        self.A, self.B = A, B
+        self.n, self.r, self.d_in, self.d_out = int(n), int(r), int(d_in), int(B.shape[1])
+        self.c = lora_pool(_ptr(A), _ptr(B), self.n, self.r, self.d_in, self.d_out, _dtype_code(A))
+
+
+class Batch:
+    """Which adapters apply to which rows (see lora_batch in include/lora.h)."""
+
+    def __init__(self, n_tokens: int, idx, seg_off=None, scale=None):
+        torch = _torch()
+        if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
+            raise LoraError(-2, "idx must be a contiguous int32 [S][K] tensor")
+        S, K = idx.shape
+        if seg_off is not None and (seg_off.dtype != torch.int32 or seg_off.numel() != S + 1):
+            raise LoraError(-2, "seg_off must be int32 [S+1]")
+        if scale is not None and (scale.dtype != torch.float32 or tuple(scale.shape) != (S, K)
+                                  or not scale.is_contiguous()):
+            raise LoraError(-2, "scale must be a contiguous float32 [S][K] tensor")
+        if seg_off is None and S != n_tokens:
+            raise LoraError(-2, "per-token mode needs idx with n_tokens rows")
+        self.idx, self.seg_off, self.scale = idx, seg_off, scale
+        self.T, self.S, self.K = int(n_tokens), int(S), int(K)
+        self.c = lora_batch(self.T, self.S, _ptr(seg_off), _ptr(idx), self.K, _ptr(scale))
+
+
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise LoraError(-2, "activations must be 2-D")
+    if t.numel() == 0:  # no rows: torch reports arbitrary strides for empty views
+        return max(int(t.shape[1]), 1)
+    if t.stride(1) != 1:
+        raise LoraError(-2, "activations must have unit column stride")
+    return int(t.stride(0))
+
+
+def lora_workspace_size(batch: Batch, n_adapters: int) -> int:
+    return int(lib().lora_workspace_size(ctypes.byref(batch.c), n_adapters))
+
+
+def new_workspace(batch: Batch, n_adapters: int, device):
+    torch = _torch()
+    nbytes = lora_workspace_size(batch, n_adapters)
+    if nbytes == 0:
+        raise LoraError(-2, "invalid batch")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def lora_plan_build(batch: Batch, n_adapters: int, plan):
+    _check(lib().lora_plan_build(ctypes.byref(batch.c), n_adapters, _ptr(plan), plan.numel(), _stream(plan)),
+           "lora_plan_build")
+
+
+def lora_apply(pool: Pool, batch: Batch, x, y, ws):
+    _check(lib().lora_apply(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(x), _ld(x), _ptr(y), _ld(y), _ptr(ws),
+                            ws.numel(), _stream(y)), "lora_apply")
+
+
+def lora_shrink(pool: Pool, batch: Batch, x, v, ws):
+    _check(lib().lora_shrink(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(x), _ld(x), _ptr(v), _ld(v),
+                             _ptr(ws), ws.numel(), _stream(v)), "lora_shrink")
+
+
+def lora_expand(pool: Pool, batch: Batch, v, y, ws):
+    _check(lib().lora_expand(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(v), _ld(v), _ptr(y), _ld(y),
+                             _ptr(ws), ws.numel(), _stream(y)), "lora_expand")
+
+
+def lora_apply_planned(pool: Pool, batch: Batch, plan, x, y):
+    _check(lib().lora_apply_planned(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), _ptr(x),
+                                    _ld(x), _ptr(y), _ld(y), _stream(y)), "lora_apply_planned")
+
+
+def lora_shrink_planned(pool: Pool, batch: Batch, plan, x, v):
+    _check(lib().lora_shrink_planned(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), _ptr(x),
+                                     _ld(x), _ptr(v), _ld(v), _stream(v)), "lora_shrink_planned")
+
+
+def lora_expand_planned(pool: Pool, batch: Batch, plan, v, y):
+    _check(lib().lora_expand_planned(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), _ptr(v),
+                                     _ld(v), _ptr(y), _ld(y), _stream(y)), "lora_expand_planned")
+
+
+def problems_table(problems: Sequence, device):
+    """Device array of lora_problem for (A, B, x, y) tuples of one shape; returns
+    (table tensor, all_aligned).  The tensors must stay alive while it is used."""
+    torch = _torch()
+    rows, aligned = [], True
+    for A, B, x, y in problems:
+        e = 8 if A.dtype == torch.bfloat16 else 4
+        ldx, ldy = _ld(x), _ld(y)
+        ptrs = [_ptr(A), _ptr(B), _ptr(x), _ptr(y)]
+        aligned &= all(p % 16 == 0 for p in ptrs) and ldx % e == 0 and ldy % e == 0
+        rows.append(ptrs + [ldx, ldy])
+    table = torch.tensor(rows, dtype=torch.int64).to(device)
+    return table, aligned
+
+
+def lora_apply_multi(shape: Pool, batch: Batch, plan, table, aligned: bool = True):
+    """shape: a Pool whose shape (n, r, d_in, d_out, dtype) all problems share."""
+    n = int(table.shape[0]) if table.numel() else 0
+    _check(lib().lora_apply_multi(ctypes.byref(shape.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), n,
+                                  _ptr(table), 1 if aligned else 0, _stream(plan)), "lora_apply_multi")
+
+
+def lora_read_device_errors(plan) -> int:
+    cnt = ctypes.c_int32(0)
+    _check(lib().lora_read_device_errors(_ptr(plan), plan.numel(), ctypes.byref(cnt), _stream(plan)),
+           "lora_read_device_errors")
+    return int(cnt.value)
+
+
+def lora_status_string(status: int) -> str:
+    return lib().lora_status_string(status).decode()
+
+
+def plan_header(plan):
+    """The plan's header words (a host copy; synchronizes)."""
+    return plan[:256].view(_torch().int32).cpu().tolist()[:16]

@@ -1,0 +1,329 @@
+// C-ABI entry points: host validation, workspace sizing, path selection and
+// launches.  No host synchronization and no allocation on any compute path.
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
+#include "lora_internal.hpp"
+
+using namespace lora;
+
+namespace {
+
+// Tuning knobs (overridable through the environment for sweeps).
+struct Tune {
+  int valu_items = 1024;  // aim for about this many VALU work items per launch
+  int valu_max_chunks = 8;
+  int mfma_items = 256;   // aim for about this many MFMA work items per launch
+  int grid_cap = 2048;    // workgroups per launch; the kernels grid-stride over items
+};
+
+int env_int(const char *name, int dflt) {
+  const char *s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+const Tune &tune() {
+  static const Tune t = [] {
+    Tune x;
+    x.valu_items = env_int("LORA_VALU_ITEMS", x.valu_items);
+    x.valu_max_chunks = env_int("LORA_VALU_MAX_CHUNKS", x.valu_max_chunks);
+    x.mfma_items = env_int("LORA_MFMA_ITEMS", x.mfma_items);
+    x.grid_cap = env_int("LORA_GRID_CAP", x.grid_cap);
+    return x;
+  }();
+  return t;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(lora_dtype d) { return d == LORA_BF16 ? 2 : 4; }
+
+struct BatchDims {
+  int T, S, K, per_token;
+};
+
+lora_status check_batch(const lora_batch *b, BatchDims &d) {
+  if (!b) return LORA_EINVAL;
+  if (b->n_tokens < 0) return LORA_ESHAPE;
+  if (b->max_slots < 1) return LORA_ESHAPE;
+  if (b->max_slots > LORA_MAX_SLOTS) return LORA_EUNSUPPORTED;
+  d.T = b->n_tokens;
+  d.K = b->max_slots;
+  d.per_token = b->seg_off == nullptr;
+  d.S = d.per_token ? d.T : b->n_segments;
+  if (d.S < 0) return LORA_ESHAPE;
+  if (d.S > 0 && !b->idx) return LORA_EINVAL;
+  if ((int64_t)d.S * d.K > INT32_MAX / 2) return LORA_EUNSUPPORTED;
+  return LORA_OK;
+}
+
+lora_status check_shape(const lora_pool *p) {
+  if (!p) return LORA_EINVAL;
+  if (p->dtype != LORA_F32 && p->dtype != LORA_BF16) return LORA_EINVAL;
+  if (p->n_adapters < 1 || p->rank < 1 || p->d_in < 1 || p->d_out < 1) return LORA_ESHAPE;
+  if (p->rank > LORA_MAX_RANK) return LORA_EUNSUPPORTED;
+  return LORA_OK;
+}
+
+lora_status check_pool(const lora_pool *p) {
+  lora_status st = check_shape(p);
+  if (st) return st;
+  if (!p->A || !p->B) return LORA_EINVAL;
+  return LORA_OK;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+size_t span_bytes(int rows, int64_t ld, int cols, int eb) {
+  if (rows <= 0) return 0;
+  return (size_t(rows - 1) * size_t(ld) + size_t(cols)) * size_t(eb);
+}
+
+struct Plan {
+  PlanLayout L;
+  PlanView V;
+};
+
+lora_status plan_for(const BatchDims &d, int n, const void *ws, size_t ws_bytes, Plan &P) {
+  P.L = plan_layout(d.S, d.T, n);
+  if (!ws) return LORA_EWORKSPACE;
+  if (ws_bytes < P.L.total) return LORA_EWORKSPACE;
+  if (!aligned16(ws)) return LORA_EINVAL;
+  P.V = plan_view(const_cast<void *>(ws), P.L, d.K, d.per_token);
+  return LORA_OK;
+}
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+int pow2_floor(int x) {
+  int p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+// Choose the launch: vector path, MFMA eligibility, chunking, grid and LDS.
+struct Launch {
+  bool vec;
+  int jt;
+  int grid;
+  size_t smem;
+};
+
+Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Plan &P, int n_problems, bool vec,
+                 ApplyArgs &a) {
+  const Tune &tn = tune();
+  const int r = shape->rank, d_out = shape->d_out;
+  Launch L;
+  L.vec = vec;
+  const bool mfma = vec && shape->dtype == LORA_BF16 && (r == 16 || r == 32 || r == 64 || r == 128) &&
+                    d.K * r <= kMfmaMaxSlotRank;
+  L.jt = mfma ? r / 16 : 0;
+
+  // output-column chunks: more chunks per tile when there are few tiles
+  const int est_v = std::max(1, std::min(d.S, shape->n_adapters)) * n_problems;
+  const int est_m = std::max(1, (d.T + kMfmaRows - 1) / kMfmaRows) * n_problems;
+  int cv = 1, cm = 1;
+  if (mode != MODE_SHRINK) {
+    cv = std::min(pow2_floor(std::max(1, tn.valu_items / est_v)), tn.valu_max_chunks);
+    cv = std::max(1, std::min(cv, std::max(1, d_out / 256)));
+    cm = pow2_floor(std::max(1, tn.mfma_items / est_m));
+    cm = std::max(1, std::min(cm, std::max(1, d_out / 512)));
+  }
+  a.wv = round_up((d_out + cv - 1) / cv, 64);
+  a.cv = (d_out + a.wv - 1) / a.wv;
+  a.wm = round_up((d_out + cm - 1) / cm, 64);
+  a.cm = (d_out + a.wm - 1) / a.wm;
+  if (mode == MODE_SHRINK) { a.cv = a.cm = 1; a.wv = a.wm = round_up(d_out, 64); }
+
+  const int64_t max_items = (int64_t)n_problems * ((int64_t)P.L.bound_m * a.cm + (int64_t)P.L.bound_v * a.cv);
+  int64_t g = std::min<int64_t>(max_items, tn.grid_cap);
+  L.grid = round_up((int)std::max<int64_t>(g, 1), 8);
+  L.smem = apply_smem_bytes(r, a.kr_max, L.jt > 0);
+  return L;
+}
+
+void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Plan &P, const lora_pool *shape) {
+  std::memset(&a, 0, sizeof(a));
+  a.seg_off = b->seg_off;
+  a.idx = b->idx;
+  a.scale = b->scale;
+  a.K = d.K;
+  a.hdr = P.V.hdr;
+  a.sseg = P.V.sseg;
+  a.sst = P.V.sst;
+  a.cumlen = P.V.cumlen;
+  a.tiles_m = P.V.tiles_m;
+  a.tiles_v = P.V.tiles_v;
+  a.n = shape->n_adapters;
+  a.r = shape->rank;
+  a.d_in = shape->d_in;
+  a.d_out = shape->d_out;
+  a.kr_max = d.K * shape->rank;
+}
+
+lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const void *ws, size_t ws_bytes,
+                bool build, const void *x, int64_t ldx, void *y, int64_t ldy, float *v, int64_t ldv,
+                hipStream_t stream) {
+  lora_status st = check_pool(pool);
+  if (st) return st;
+  BatchDims d;
+  if ((st = check_batch(batch, d))) return st;
+  if ((int64_t)d.K * pool->rank > LORA_MAX_SLOT_RANK) return LORA_EUNSUPPORTED;
+  const int eb = elem_bytes(pool->dtype);
+  const bool need_x = mode != MODE_EXPAND, need_y = mode != MODE_SHRINK, need_v = mode != MODE_FUSED;
+  if (d.T > 0) {
+    if (need_x && !x) return LORA_EINVAL;
+    if (need_y && !y) return LORA_EINVAL;
+    if (need_v && !v) return LORA_EINVAL;
+  }
+  if (need_x && ldx < pool->d_in) return LORA_ESHAPE;
+  if (need_y && ldy < pool->d_out) return LORA_ESHAPE;
+  if (need_v && ldv < (int64_t)d.K * pool->rank) return LORA_ESHAPE;
+  const size_t xs = need_x ? span_bytes(d.T, ldx, pool->d_in, eb) : 0;
+  const size_t ys = need_y ? span_bytes(d.T, ldy, pool->d_out, eb) : 0;
+  const size_t vs = need_v ? span_bytes(d.T, ldv, d.K * pool->rank, 4) : 0;
+  if (overlap(x, xs, y, ys) || overlap(v, vs, x, xs) || overlap(v, vs, y, ys)) return LORA_EINVAL;
+  Plan P;
+  if ((st = plan_for(d, pool->n_adapters, ws, ws_bytes, P))) return st;
+  if (overlap(ws, P.L.total, x, xs) || overlap(ws, P.L.total, y, ys) || overlap(ws, P.L.total, v, vs))
+    return LORA_EINVAL;
+
+  if (build) {
+    if (launch_plan(P.V, batch->seg_off, batch->idx, stream) != hipSuccess) return LORA_EHIP;
+  }
+  if (d.T == 0 || d.S == 0) return LORA_OK;
+
+  const int E = pool->dtype == LORA_BF16 ? 8 : 4;
+  bool vec = aligned16(pool->A) && aligned16(pool->B) && pool->d_in % E == 0 && pool->d_out % E == 0 &&
+             pool->rank % E == 0;
+  if (need_x) vec = vec && aligned16(x) && ldx % E == 0;
+  if (need_y) vec = vec && aligned16(y) && ldy % E == 0;
+  if (need_v) vec = vec && aligned16(v) && ldv % 4 == 0;
+
+  ApplyArgs a;
+  fill_common(a, batch, d, P, pool);
+  a.single.A = pool->A;
+  a.single.B = pool->B;
+  a.single.x = x;
+  a.single.y = y;
+  a.single.ldx = ldx;
+  a.single.ldy = ldy;
+  a.probs = nullptr;
+  a.n_problems = 1;
+  a.v = v;
+  a.ldv = ldv;
+  const Launch L = configure(mode, pool, d, P, 1, vec, a);
+  if (launch_apply(mode, pool->dtype, L.vec, L.jt, a, L.grid, L.smem, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_abi_version(void) { return 100; }
+
+const char *lora_status_string(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "ok";
+    case LORA_EINVAL: return "invalid argument (NULL pointer, overlapping buffers or bad enum)";
+    case LORA_ESHAPE: return "invalid shape (non-positive size, ld < d or bad counts)";
+    case LORA_EWORKSPACE: return "workspace missing or too small";
+    case LORA_EUNSUPPORTED: return "unsupported rank, slot count or size";
+    case LORA_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t lora_workspace_size(const lora_batch *batch, int32_t n_adapters) {
+  BatchDims d;
+  if (check_batch(batch, d) != LORA_OK || n_adapters < 1) return 0;
+  return plan_layout(d.S, d.T, n_adapters).total;
+}
+
+lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  BatchDims d;
+  lora_status st = check_batch(batch, d);
+  if (st) return st;
+  if (n_adapters < 1) return LORA_ESHAPE;
+  Plan P;
+  if ((st = plan_for(d, n_adapters, ws, ws_bytes, P))) return st;
+  if (launch_plan(P.V, batch->seg_off, batch->idx, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
+lora_status lora_apply(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
+                       int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return run(MODE_FUSED, pool, batch, ws, ws_bytes, true, x, ldx, y, ldy, nullptr, 0, stream);
+}
+
+lora_status lora_shrink(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, float *v,
+                        int64_t ldv, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return run(MODE_SHRINK, pool, batch, ws, ws_bytes, true, x, ldx, nullptr, 0, v, ldv, stream);
+}
+
+lora_status lora_expand(const lora_pool *pool, const lora_batch *batch, const float *v, int64_t ldv, void *y,
+                        int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return run(MODE_EXPAND, pool, batch, ws, ws_bytes, true, nullptr, 0, y, ldy, const_cast<float *>(v), ldv, stream);
+}
+
+lora_status lora_apply_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                               const void *x, int64_t ldx, void *y, int64_t ldy, hipStream_t stream) {
+  return run(MODE_FUSED, pool, batch, plan, plan_bytes, false, x, ldx, y, ldy, nullptr, 0, stream);
+}
+
+lora_status lora_shrink_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                                const void *x, int64_t ldx, float *v, int64_t ldv, hipStream_t stream) {
+  return run(MODE_SHRINK, pool, batch, plan, plan_bytes, false, x, ldx, nullptr, 0, v, ldv, stream);
+}
+
+lora_status lora_expand_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                                const float *v, int64_t ldv, void *y, int64_t ldy, hipStream_t stream) {
+  return run(MODE_EXPAND, pool, batch, plan, plan_bytes, false, nullptr, 0, y, ldy, const_cast<float *>(v), ldv,
+             stream);
+}
+
+lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                             int32_t n_problems, const lora_problem *problems, int32_t problems_aligned,
+                             hipStream_t stream) {
+  lora_status st = check_shape(shape);
+  if (st) return st;
+  BatchDims d;
+  if ((st = check_batch(batch, d))) return st;
+  if ((int64_t)d.K * shape->rank > LORA_MAX_SLOT_RANK) return LORA_EUNSUPPORTED;
+  if (n_problems < 0) return LORA_ESHAPE;
+  if (n_problems > 0 && !problems) return LORA_EINVAL;
+  if (!aligned16(problems)) return LORA_EINVAL;
+  Plan P;
+  if ((st = plan_for(d, shape->n_adapters, plan, plan_bytes, P))) return st;
+  if (n_problems == 0 || d.T == 0 || d.S == 0) return LORA_OK;
+  const int E = shape->dtype == LORA_BF16 ? 8 : 4;
+  const bool vec = problems_aligned && shape->d_in % E == 0 && shape->d_out % E == 0 && shape->rank % E == 0;
+  ApplyArgs a;
+  fill_common(a, batch, d, P, shape);
+  a.probs = problems;
+  a.n_problems = n_problems;
+  const Launch L = configure(MODE_FUSED, shape, d, P, n_problems, vec, a);
+  if (launch_apply(MODE_FUSED, shape->dtype, L.vec, L.jt, a, L.grid, L.smem, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
+lora_status lora_read_device_errors(const void *plan, size_t plan_bytes, int32_t *count, hipStream_t stream) {
+  if (!plan || !count) return LORA_EINVAL;
+  if (plan_bytes < sizeof(int) * H_WORDS) return LORA_EWORKSPACE;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, static_cast<const int *>(plan) + H_ERR, sizeof(v), hipMemcpyDeviceToHost, stream) !=
+      hipSuccess)
+    return LORA_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LORA_EHIP;
+  *count = v;
+  return LORA_OK;
+}
+
+}  // extern "C"

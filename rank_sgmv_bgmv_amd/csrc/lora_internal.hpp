@@ -1,0 +1,132 @@
+// Internal declarations shared by the plan (scheduler) kernel, the apply
+// kernels and the C-ABI host entry points.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lora.h"
+
+namespace lora {
+
+constexpr int kPlanThreads = 1024;  // one workgroup builds the plan
+constexpr int kThreads = 256;       // apply kernels: 4 wave64s per workgroup
+constexpr int kMfmaRows = 64;       // rows per MFMA tile (16 per wave)
+constexpr int kValuRows = 16;       // rows per VALU tile
+constexpr int kMfmaMinRows = 17;    // adapter groups with at least this many rows get MFMA tiles
+constexpr int kRowBlock = 8;        // rows per VALU pass
+constexpr int kValuOutChunk = 512;  // outputs per VALU expand sub-chunk (LDS staging of the delta)
+constexpr int kMfmaMaxRank = 128;   // MFMA tiles serve ranks 16, 32, 64, 128
+constexpr int kMfmaMaxSlotRank = 512;
+
+// Plan header words (int32).
+enum {
+  H_TILES_M = 0,   // number of MFMA tiles
+  H_TILES_V = 1,   // number of VALU tiles
+  H_ERR = 2,       // invalid indices + offset violations met by the last build
+  H_ACTIVE = 3,    // requests with at least one row and one valid slot
+  H_GROUPS = 4,    // adapter groups
+  H_ROWS = 5,      // rows covered by active requests
+  H_N = 6, H_S = 7, H_T = 8, H_K = 9,
+  H_MAGIC = 10,
+  H_WORDS = 64
+};
+constexpr int kPlanMagic = 0x4c6f5241;  // "LoRA"
+
+// Byte offsets of the plan arrays inside the workspace.
+struct PlanLayout {
+  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, tiles_m, tiles_v, total;
+  int S, T, n, bound_m, bound_v;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline PlanLayout plan_layout(int S, int T, int n) {
+  PlanLayout L{};
+  L.S = S; L.T = T; L.n = n;
+  L.bound_m = (T + kMfmaRows - 1) / kMfmaRows + S + 1;
+  L.bound_v = (T + kValuRows - 1) / kValuRows + S + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  L.hdr = take(sizeof(int) * H_WORDS);
+  L.start = take(sizeof(int) * (size_t(S) + 1));
+  L.key = take(sizeof(int) * (size_t(S) + 1));
+  L.cnt = take(sizeof(int) * (size_t(n) + 2));
+  L.cur = take(sizeof(int) * (size_t(n) + 2));
+  L.sseg = take(sizeof(int) * (size_t(S) + 1));
+  L.sst = take(sizeof(int) * (size_t(S) + 1));
+  L.cumlen = take(sizeof(int) * (size_t(S) + 2));
+  L.gtmp = take(sizeof(int) * (size_t(S) + 2));
+  L.gstart = take(sizeof(int) * (size_t(S) + 2));
+  L.toff_m = take(sizeof(int) * (size_t(S) + 2));
+  L.toff_v = take(sizeof(int) * (size_t(S) + 2));
+  L.tiles_m = take(sizeof(int4) * size_t(L.bound_m));
+  L.tiles_v = take(sizeof(int4) * size_t(L.bound_v));
+  L.total = off;
+  return L;
+}
+
+// Device view of a plan.
+struct PlanView {
+  int *hdr, *start, *key, *cnt, *cur, *sseg, *sst, *cumlen, *gtmp, *gstart, *toff_m, *toff_v;
+  int4 *tiles_m, *tiles_v;
+  int S, T, n, K, per_token;
+};
+
+inline PlanView plan_view(void *ws, const PlanLayout &L, int K, int per_token) {
+  char *b = static_cast<char *>(ws);
+  PlanView P;
+  P.hdr = reinterpret_cast<int *>(b + L.hdr);
+  P.start = reinterpret_cast<int *>(b + L.start);
+  P.key = reinterpret_cast<int *>(b + L.key);
+  P.cnt = reinterpret_cast<int *>(b + L.cnt);
+  P.cur = reinterpret_cast<int *>(b + L.cur);
+  P.sseg = reinterpret_cast<int *>(b + L.sseg);
+  P.sst = reinterpret_cast<int *>(b + L.sst);
+  P.cumlen = reinterpret_cast<int *>(b + L.cumlen);
+  P.gtmp = reinterpret_cast<int *>(b + L.gtmp);
+  P.gstart = reinterpret_cast<int *>(b + L.gstart);
+  P.toff_m = reinterpret_cast<int *>(b + L.toff_m);
+  P.toff_v = reinterpret_cast<int *>(b + L.toff_v);
+  P.tiles_m = reinterpret_cast<int4 *>(b + L.tiles_m);
+  P.tiles_v = reinterpret_cast<int4 *>(b + L.tiles_v);
+  P.S = L.S; P.T = L.T; P.n = L.n; P.K = K; P.per_token = per_token;
+  return P;
+}
+
+enum Mode { MODE_FUSED = 0, MODE_SHRINK = 1, MODE_EXPAND = 2 };
+
+struct ApplyArgs {
+  // batch
+  const int *seg_off;
+  const int *idx;
+  const float *scale;
+  int K;
+  // plan (read only)
+  const int *hdr, *sseg, *sst, *cumlen;
+  const int4 *tiles_m, *tiles_v;
+  // shape shared by every problem
+  int n, r, d_in, d_out;
+  // problems
+  lora_problem single;
+  const lora_problem *probs;  // device array, or nullptr => `single`
+  int n_problems;
+  // output-column chunks per tile kind: cm chunks of wm columns (MFMA tiles), cv of wv (VALU tiles)
+  int cm, wm, cv, wv;
+  // split API: float32 intermediate [T][ldv]
+  float *v;
+  int64_t ldv;
+  // layout of dynamic LDS
+  int kr_max;      // max_slots * rank (row stride of the VALU intermediate)
+};
+
+size_t apply_smem_bytes(int r, int kr_max, bool mfma);
+
+hipError_t launch_plan(const PlanView &P, const int *seg_off, const int *idx, hipStream_t stream);
+
+// dtype: LORA_F32 / LORA_BF16; vec: 16-byte vector path; jt: rank/16 for MFMA tiles (0 = no MFMA).
+hipError_t launch_apply(int mode, int dtype, bool vec, int jt, const ApplyArgs &args, int grid, size_t smem,
+                        hipStream_t stream);
+
+}  // namespace lora

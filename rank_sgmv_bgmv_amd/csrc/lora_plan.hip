@@ -1,0 +1,254 @@
+// Segment / index scheduler: groups the requests of a batch by adapter and
+// cuts every group into row tiles for the apply kernels.
+//
+// "Serving several LoRAs, ControlNet and IP-Adapter", "Exercises" (the answer
+// on four requests with four LoRAs): group the batch's activations by LoRA
+// index, let one kernel handle every group, add the results back in the
+// original order; requests that share a LoRA fall into one group, which makes
+// the product larger and denser.  "Punica: Multi-Tenant LoRA Serving"
+// (contribution 1) is the same segmented-gather idea.
+//
+// The plan is built on the device by one workgroup, so indices and offsets
+// never travel to the host.  Steps:
+//   1. sanitise offsets: start[s] = clamp(max(seg_off[0..s]), 0, T), which
+//      makes requests disjoint whatever the input; violations are counted;
+//   2. key every request: its only valid adapter, or a shared "multi" key n
+//      when it stacks several adapters (each such request is its own group),
+//      or none when it has no rows or no valid slot; invalid indices counted;
+//   3. counting sort of requests by key (histogram, scan, scatter);
+//   4. prefix sums of the sorted requests' lengths (rows in sorted order);
+//   5. group boundaries; a group of >= kMfmaMinRows rows is cut into MFMA
+//      tiles of kMfmaRows rows, a smaller one into VALU tiles of kValuRows;
+//   6. one tile descriptor per tile: {first row, first request, rows, group end}.
+// Rows never move: a tile names rows by (sorted request, offset) and the apply
+// kernels read and write x / y rows in place.
+
+#include <climits>
+
+#include "lora_internal.hpp"
+
+namespace lora {
+namespace {
+
+__device__ __forceinline__ int wave_incl_scan_add(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_max(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o);
+    if (lane >= o) v = max(v, u);
+  }
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over the 1024-thread block.
+__device__ int block_excl_scan_add(int v, int *sh, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_incl_scan_add(v);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < 16 ? sh[lane] : 0;
+    const int ti = wave_incl_scan_add(t);
+    if (lane < 16) sh[lane] = ti - t;
+    if (lane == 15) sh[16] = ti;
+  }
+  __syncthreads();
+  const int res = inc - v + sh[w];
+  total = sh[16];
+  __syncthreads();
+  return res;
+}
+
+// Inclusive prefix max of one value per thread over the block.
+__device__ int block_incl_scan_max(int v, int *sh, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_incl_scan_max(v);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < 16 ? sh[lane] : INT_MIN;
+    const int ti = wave_incl_scan_max(t);
+    if (lane < 16) sh[lane] = ti;  // inclusive max of waves 0..lane
+  }
+  __syncthreads();
+  const int res = w > 0 ? max(inc, sh[w - 1]) : inc;
+  total = sh[15];
+  __syncthreads();
+  return res;
+}
+
+// out[i] = sum_{j<i} in[i]; in and out may alias.  Returns the total.
+__device__ int chunked_excl_scan(const int *in, int *out, int N, int *sh) {
+  int carry = 0;
+  for (int base = 0; base < N; base += kPlanThreads) {
+    const int i = base + threadIdx.x;
+    const int v = i < N ? in[i] : 0;
+    int tot;
+    const int ex = block_excl_scan_add(v, sh, tot);
+    if (i < N) out[i] = carry + ex;
+    carry += tot;
+  }
+  return carry;
+}
+
+// Largest g in [lo, hi] with a[g] <= key (a non-decreasing, a[lo] <= key).
+__device__ __forceinline__ int last_le(const int *a, int lo, int hi, int key) {
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= key) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const int *__restrict__ seg_off,
+                                                            const int *__restrict__ idx) {
+  __shared__ int sh[20];
+  __shared__ int s_err;
+  const int tid = threadIdx.x;
+  const int S = P.S, T = P.T, n = P.n, K = P.K;
+
+  if (tid == 0) s_err = 0;
+  for (int b = tid; b <= n; b += kPlanThreads) P.cnt[b] = 0;
+  __syncthreads();
+
+  // 1. sanitised request starts, start[S] = end of the last request.
+  if (P.per_token) {
+    for (int s = tid; s <= S; s += kPlanThreads) P.start[s] = s;
+  } else {
+    int carry = 0;
+    for (int base = 0; base <= S; base += kPlanThreads) {
+      const int s = base + tid;
+      int v = INT_MIN;
+      if (s <= S) {
+        v = seg_off[s];
+        int bad = 0;
+        if (s == 0 && v < 0) bad = 1;
+        if (s == S && v > T) bad = 1;
+        if (s > 0 && v < seg_off[s - 1]) bad = 1;
+        if (bad) atomicAdd(&s_err, 1);
+      }
+      int tot;
+      const int m = block_incl_scan_max(v, sh, tot);
+      if (s <= S) P.start[s] = min(max(max(m, carry), 0), T);
+      carry = max(carry, tot);
+    }
+  }
+  __syncthreads();
+
+  // 2. keys and histogram.
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int len = P.start[s + 1] - P.start[s];
+    int nact = 0, a0 = -1;
+    for (int k = 0; k < K; ++k) {
+      const int a = idx[(int64_t)s * K + k];
+      if (a == -1) continue;
+      if (a < -1 || a >= n) { atomicAdd(&s_err, 1); continue; }
+      if (nact == 0) a0 = a;
+      ++nact;
+    }
+    const int key = (len <= 0 || nact == 0) ? -1 : (nact == 1 ? a0 : n);
+    P.key[s] = key;
+    if (key >= 0) atomicAdd(&P.cnt[key], 1);
+  }
+  __syncthreads();
+
+  // 3. bucket starts, then scatter (order inside a bucket is not significant).
+  const int n_active = chunked_excl_scan(P.cnt, P.cur, n + 1, sh);
+  __syncthreads();
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int key = P.key[s];
+    if (key >= 0) P.sseg[atomicAdd(&P.cur[key], 1)] = s;
+  }
+  __syncthreads();
+
+  // 4. rows in sorted order.
+  for (int q = tid; q < n_active; q += kPlanThreads) {
+    const int s = P.sseg[q];
+    P.sst[q] = P.start[s];
+    P.cumlen[q] = P.start[s + 1] - P.start[s];
+  }
+  __syncthreads();
+  const int total_rows = chunked_excl_scan(P.cumlen, P.cumlen, n_active, sh);
+  if (tid == 0) P.cumlen[n_active] = total_rows;
+  __syncthreads();
+
+  // 5. groups: a new group starts where the key changes; every multi-adapter request is its own group.
+  for (int q = tid; q < n_active; q += kPlanThreads) {
+    const int kq = P.key[P.sseg[q]];
+    P.gtmp[q] = (q == 0 || kq == n || kq != P.key[P.sseg[q - 1]]) ? 1 : 0;
+  }
+  __syncthreads();
+  for (int q = tid; q < n_active; q += kPlanThreads) P.gstart[q] = P.gtmp[q];  // keep flags
+  __syncthreads();
+  const int n_groups = chunked_excl_scan(P.gtmp, P.gtmp, n_active, sh);
+  __syncthreads();
+  // gstart currently holds the flags; write starts into toff_m temporarily, then copy.
+  for (int q = tid; q < n_active; q += kPlanThreads)
+    if (P.gstart[q]) P.toff_m[P.gtmp[q]] = q;
+  __syncthreads();
+  for (int g = tid; g < n_groups; g += kPlanThreads) P.gstart[g] = P.toff_m[g];
+  if (tid == 0) P.gstart[n_groups] = n_active;
+  __syncthreads();
+
+  // tiles per group
+  for (int g = tid; g < n_groups; g += kPlanThreads) {
+    const int rows = P.cumlen[P.gstart[g + 1]] - P.cumlen[P.gstart[g]];
+    const bool big = rows >= kMfmaMinRows;
+    P.toff_m[g] = big ? (rows + kMfmaRows - 1) / kMfmaRows : 0;
+    P.toff_v[g] = big ? 0 : (rows + kValuRows - 1) / kValuRows;
+  }
+  __syncthreads();
+  const int nt_m = chunked_excl_scan(P.toff_m, P.toff_m, n_groups, sh);
+  const int nt_v = chunked_excl_scan(P.toff_v, P.toff_v, n_groups, sh);
+  if (tid == 0) { P.toff_m[n_groups] = nt_m; P.toff_v[n_groups] = nt_v; }
+  __syncthreads();
+
+  // 6. tile descriptors
+  for (int u = tid; u < nt_m + nt_v; u += kPlanThreads) {
+    const bool is_m = u < nt_m;
+    const int uu = is_m ? u : u - nt_m;
+    const int *toff = is_m ? P.toff_m : P.toff_v;
+    const int rows_per = is_m ? kMfmaRows : kValuRows;
+    const int g = last_le(toff, 0, n_groups - 1, uu);
+    const int gs = P.gstart[g], ge = P.gstart[g + 1];
+    const int p0 = P.cumlen[gs] + (uu - toff[g]) * rows_per;
+    const int nrows = min(rows_per, P.cumlen[ge] - p0);
+    const int q0 = last_le(P.cumlen, gs, ge - 1, p0);
+    const int4 d = make_int4(p0, q0, nrows, ge);
+    if (is_m) P.tiles_m[uu] = d; else P.tiles_v[uu] = d;
+  }
+
+  __syncthreads();
+  if (tid == 0) {
+    P.hdr[H_TILES_M] = nt_m;
+    P.hdr[H_TILES_V] = nt_v;
+    P.hdr[H_ERR] = s_err;
+    P.hdr[H_ACTIVE] = n_active;
+    P.hdr[H_GROUPS] = n_groups;
+    P.hdr[H_ROWS] = total_rows;
+    P.hdr[H_N] = n;
+    P.hdr[H_S] = S;
+    P.hdr[H_T] = T;
+    P.hdr[H_K] = K;
+    P.hdr[H_MAGIC] = kPlanMagic;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanView &P, const int *seg_off, const int *idx, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, P, seg_off, idx);
+  return hipGetLastError();
+}
+
+}  // namespace lora

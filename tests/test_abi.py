@@ -1,0 +1,121 @@
+"""The C-ABI library loads and exports what include/lora.h declares; host-side
+validation returns the documented status codes without launching anything.
+CPU only: no call here reaches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_sgmv_bgmv_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from rank_sgmv_bgmv_amd import build
+        build.build()
+    return L.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in lora.h but not exported"
+
+
+def test_exported_symbols_match_binding(lib):
+    for name in declared_functions():
+        assert hasattr(L, name) or name in ("lora_abi_version",), f"binding lacks {name}"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.lora_abi_version() == 100
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.lora_status_string(st)
+    assert b"workspace" in lib.lora_status_string(-3)
+
+
+FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def _pool(**kw):
+    args = dict(A=FAKE, B=FAKE * 2, n_adapters=4, rank=8, d_in=64, d_out=64, dtype=L.LORA_BF16)
+    args.update(kw)
+    return L.lora_pool(args["A"], args["B"], args["n_adapters"], args["rank"], args["d_in"], args["d_out"], args["dtype"])
+
+
+def _batch(**kw):
+    args = dict(n_tokens=10, n_segments=3, seg_off=FAKE * 3, idx=FAKE * 4, max_slots=1, scale=None)
+    args.update(kw)
+    return L.lora_batch(args["n_tokens"], args["n_segments"], args["seg_off"], args["idx"], args["max_slots"], args["scale"])
+
+
+def test_workspace_size(lib):
+    b = _batch()
+    n = lib.lora_workspace_size(ctypes.byref(b), 4)
+    assert n > 0 and n % 256 == 0
+    assert lib.lora_workspace_size(ctypes.byref(_batch(n_tokens=-1)), 4) == 0
+    assert lib.lora_workspace_size(ctypes.byref(_batch(max_slots=0)), 4) == 0
+    assert lib.lora_workspace_size(ctypes.byref(b), 0) == 0
+    big = lib.lora_workspace_size(ctypes.byref(_batch(n_tokens=100000, n_segments=5000)), 1000)
+    assert big > n
+
+
+def _apply(lib, pool, batch, x=FAKE * 5, ldx=64, y=FAKE * 1000, ldy=64, ws=FAKE * 2000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.lora_workspace_size(ctypes.byref(batch), pool.n_adapters) or 1 << 20
+    return lib.lora_apply(ctypes.byref(pool), ctypes.byref(batch), x, ldx, y, ldy, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(pool=dict(A=None)), -1),
+    (dict(pool=dict(dtype=7)), -1),
+    (dict(pool=dict(rank=0)), -2),
+    (dict(pool=dict(rank=257)), -4),
+    (dict(pool=dict(d_in=0)), -2),
+    (dict(pool=dict(n_adapters=0)), -2),
+    (dict(batch=dict(n_tokens=-1)), -2),
+    (dict(batch=dict(max_slots=9)), -4),
+    (dict(batch=dict(max_slots=0)), -2),
+    (dict(batch=dict(idx=None)), -1),
+    (dict(batch=dict(n_segments=-2)), -2),
+    (dict(pool=dict(rank=256), batch=dict(max_slots=8)), -4),
+    (dict(ldx=63), -2),
+    (dict(ldy=10), -2),
+    (dict(x=None), -1),
+    (dict(y=None), -1),
+    (dict(y=FAKE * 5 + 64), -1),            # y overlaps x
+    (dict(ws=None), -3),
+    (dict(ws_bytes=100), -3),
+])
+def test_apply_validation(lib, case, expect):
+    pool = _pool(**case.get("pool", {}))
+    batch = _batch(**case.get("batch", {}))
+    kw = {k: v for k, v in case.items() if k not in ("pool", "batch")}
+    assert _apply(lib, pool, batch, **kw) == expect
+
+
+def test_split_and_multi_validation(lib):
+    pool, batch = _pool(), _batch()
+    ws_bytes = lib.lora_workspace_size(ctypes.byref(batch), 4)
+    # ldv < K * rank
+    assert lib.lora_shrink(ctypes.byref(pool), ctypes.byref(batch), FAKE, 64, FAKE * 1000, 7, FAKE * 2000, ws_bytes, None) == -2
+    assert lib.lora_expand(ctypes.byref(pool), ctypes.byref(batch), None, 8, FAKE * 1000, 64, FAKE * 2000, ws_bytes, None) == -1
+    assert lib.lora_apply_multi(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, None, 1, None) == -1
+    assert lib.lora_apply_multi(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, 16, 2, FAKE, 1, None) == -3
+    assert lib.lora_apply_multi(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, -1, FAKE, 1, None) == -2
+    assert lib.lora_plan_build(ctypes.byref(batch), 0, FAKE * 2000, ws_bytes, None) == -2
+    assert lib.lora_plan_build(ctypes.byref(batch), 4, FAKE * 2000, 16, None) == -3
+    cnt = ctypes.c_int32(0)
+    assert lib.lora_read_device_errors(None, 1 << 20, ctypes.byref(cnt), None) == -1

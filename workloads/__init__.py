@@ -219,12 +219,17 @@ def case_c2(seed: int = SEEDS["C2"], n: int = 1000) -> Case:
     return Case("C2", BF16, batch, pool, x, y)
 
 
-def case_c3(seed: int = SEEDS["C3"]) -> Case:
-    rng = np.random.default_rng(seed)
-    S, n = 32, 8
+def batch_c3(rng, S=32, n=8) -> Batch:
+    """32 segments of U{128..1024} tokens, each on a uniformly drawn adapter."""
     lengths = rng.integers(128, 1025, size=S)
     idx = rng.integers(0, n, size=(S, 1)).astype(np.int32)
-    batch = Batch(int(lengths.sum()), S, 1, offsets_from_lengths(lengths), idx, None)
+    return Batch(int(lengths.sum()), S, 1, offsets_from_lengths(lengths), idx, None)
+
+
+def case_c3(seed: int = SEEDS["C3"]) -> Case:
+    rng = np.random.default_rng(seed)
+    n = 8
+    batch = batch_c3(rng, 32, n)
     pool = make_pool(rng, BF16, n, 64, 4096, 4096)
     x, y = make_xy(rng, BF16, batch.T, 4096, 4096)
     return Case("C3", BF16, batch, pool, x, y)
