@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the unmerged multi-LoRA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME[,NAME]] [--no-cpu-baseline]
+
+One JSON line on stdout.  The headline workload ("C2x32") is the decode
+batch of the Llama-3-8B q_proj configuration -- 64 requests x 1 token,
+adapters drawn Zipf(1.1) from a pool of 1000 resident rank-16 adapters per
+layer, 4096 -> 4096, bf16 -- taken through the q_proj LoRA of all 32 layers:
+one step = one plan build (device scheduler) + one multi-problem fused
+launch over the 32 layer pools.  Every step uses a different batch (cycled
+from 16 seeded batches) so that adapter reuse across steps is what Zipf
+popularity gives, not a replay of one batch.
+
+`value` is LoRA-delta tokens/s (tokens through all 32 layers per second).
+`roofline` is for the dominant kernel (the fused apply kernel): algorithmic
+bytes per launch / its average duration from HIP events recorded around it
+on its stream, against the 8 TB/s HBM peak.  `variants` holds the same
+measurements for the other workloads (tiny fp32, single-layer decode, long
+prefill, the full Llama-3-8B-shaped stack, the diffusion multi-adapter
+cases).  `cpu_baseline` times the fp64 oracle on a bounded sample of the
+headline workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+from rank_sgmv_bgmv_amd import accounting  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ helpers --
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev_bf16(a, dev):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def dev_tensor(a, dtype, dev):
+    torch = torch_mod()
+    if dtype == W.BF16:
+        return dev_bf16(a, dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def dev_batch(b: W.Batch, dev):
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    idx = torch.from_numpy(np.ascontiguousarray(b.idx, dtype=np.int32)).to(dev)
+    seg = None if b.seg_off is None else torch.from_numpy(np.ascontiguousarray(b.seg_off, dtype=np.int32)).to(dev)
+    sc = None if b.scale is None else torch.from_numpy(np.ascontiguousarray(b.scale, dtype=np.float32)).to(dev)
+    return L.Batch(b.T, idx, seg, sc)
+
+
+def randn_pool(gen, n, r, d_in, d_out, dev, std=0.02):
+    """A resident bf16 pool drawn on the device (torch generator, seeded)."""
+    torch = torch_mod()
+    A = (torch.randn((n, r, d_in), generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+    B = (torch.randn((n, d_out, r), generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+    return A, B
+
+
+def randn_act(gen, T, d, dev):
+    torch = torch_mod()
+    return torch.randn((T, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+
+class Timer:
+    """Times K steps between two synchronizations; HIP events around the
+    dominant kernel's launches give its average duration."""
+
+    def __init__(self, steps):
+        torch = torch_mod()
+        self.steps = steps
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def run(self, step, warmup):
+        torch = torch_mod()
+        for i in range(warmup):
+            step(i, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(self.steps):
+            step(i, self.ev[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k_ms = [a.elapsed_time(b) for a, b in self.ev]
+        return wall, float(np.mean(k_ms)), k_ms
+
+
+def result(name, wall, steps, tokens, bytes_step, flops_step, k_ms_avg, k_bytes, k_flops, launches, extra=None):
+    ms = wall / steps * 1e3
+    d = {
+        "workload": name,
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": tokens / (ms * 1e-3),
+        "algorithmic_GBps_step": bytes_step / (ms * 1e-3) / 1e9,
+        "algorithmic_TFLOPs_step": flops_step / (ms * 1e-3) / 1e12,
+        "apply_kernel_us": round(k_ms_avg * 1e3, 3),
+        "apply_launches_per_step": launches,
+        "apply_bytes_per_launch": k_bytes,
+        "apply_GBps": k_bytes / (k_ms_avg * 1e-3) / 1e9,
+        "apply_frac_hbm": k_bytes / (k_ms_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "apply_TFLOPs": k_flops / (k_ms_avg * 1e-3) / 1e12,
+    }
+    if extra:
+        d.update(extra)
+    return d
+
+
+# ---------------------------------------------------------------- workloads --
+def bench_decode_layers(dev, steps, warmup, layers=32, n=1000, n_batches=16, seed=W.SEEDS["C2"]):
+    """C2 batch through `layers` q_proj pools: plan + one multi-problem launch per step."""
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    r, d = 16, 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    pools = [randn_pool(gen, n, r, d, d, dev) for _ in range(layers)]
+    xs = [randn_act(gen, 64, d, dev) for _ in range(layers)]
+    ys = [randn_act(gen, 64, d, dev) for _ in range(layers)]
+    batches = [W.batch_c2(np.random.default_rng([seed, j]), n) for j in range(n_batches)]
+    dbs = [dev_batch(b, dev) for b in batches]
+    plan = L.new_workspace(dbs[0], n, dev)
+    shape = L.Pool(pools[0][0], pools[0][1])
+    table, aligned = L.problems_table([(A, B, x, y) for (A, B), x, y in zip(pools, xs, ys)], dev)
+    assert aligned
+
+    def step(i, ev):
+        db = dbs[i % n_batches]
+        L.lora_plan_build(db, n, plan)
+        if ev: ev[0].record()
+        L.lora_apply_multi(shape, db, plan, table, aligned)
+        if ev: ev[1].record()
+
+    tm = Timer(steps)
+    wall, k_ms, _ = tm.run(step, warmup)
+    used = [batches[i % n_batches] for i in range(steps)]
+    distinct = np.mean([len(np.unique(b.idx)) for b in used])
+    k_bytes = layers * accounting.call_bytes(64, distinct, r, d, d, 2)
+    k_flops = layers * accounting.lora_flops(64, r, d, d)
+    res = result(f"decode q_proj x{layers} layers", wall, steps, 64, k_bytes, k_flops, k_ms, k_bytes, k_flops, 1,
+                 {"distinct_adapters_per_layer": float(distinct), "layers": layers})
+    return res, (pools, batches, xs, ys)
+
+
+def bench_single(case: W.Case, dev, steps, warmup, name):
+    """One adapted layer: plan + fused apply per step (lora_apply builds the plan)."""
+    import rank_sgmv_bgmv_amd as L
+    A, B = dev_tensor(case.pool.A, case.dtype, dev), dev_tensor(case.pool.B, case.dtype, dev)
+    pool = L.Pool(A, B)
+    db = dev_batch(case.batch, dev)
+    x = dev_tensor(case.x, case.dtype, dev)
+    y = dev_tensor(case.y, case.dtype, dev)
+    plan = L.new_workspace(db, case.pool.n, dev)
+
+    def step(i, ev):
+        L.lora_plan_build(db, case.pool.n, plan)
+        if ev: ev[0].record()
+        L.lora_apply_planned(pool, db, plan, x, y)
+        if ev: ev[1].record()
+
+    wall, k_ms, _ = Timer(steps).run(step, warmup)
+    eb = 2 if case.dtype == W.BF16 else 4
+    p = case.pool
+    touched, slot_tokens, distinct = accounting.batch_work(case.batch.seg_bounds(), case.batch.idx, p.n)
+    k_bytes = accounting.call_bytes(touched, distinct, p.r, p.d_in, p.d_out, eb)
+    k_flops = accounting.lora_flops(slot_tokens, p.r, p.d_in, p.d_out)
+    return result(name, wall, steps, touched, k_bytes, k_flops, k_ms, k_bytes, k_flops, 1,
+                  {"tokens": touched, "distinct_adapters": distinct})
+
+
+def bench_c4_stack(dev, steps, warmup, seed=W.SEEDS["C4"]):
+    """Full Llama-3-8B-shaped stack: 32 layers x 7 projections, r=32, 256 adapters per
+    projection; mixed 4 x 512 prefill + 256 decode tokens.  One plan per step, then
+    one multi-problem launch per projection shape (q,o | k,v | gate,up | down)."""
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    r, n, layers = 32, 256, W.LLAMA3_8B_LAYERS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    batch = W.batch_c4(np.random.default_rng(seed), n)
+    db = dev_batch(batch, dev)
+    T = batch.T
+    groups = {}
+    for li in range(layers):
+        for name, d_in, d_out in W.LLAMA3_8B_PROJ:
+            A, B = randn_pool(gen, n, r, d_in, d_out, dev)
+            x, y = randn_act(gen, T, d_in, dev), randn_act(gen, T, d_out, dev)
+            groups.setdefault((d_in, d_out), []).append((A, B, x, y))
+    launches = []
+    for (d_in, d_out), probs in groups.items():
+        table, aligned = L.problems_table(probs, dev)
+        launches.append((L.Pool(probs[0][0], probs[0][1]), table, aligned, probs, d_in, d_out))
+    plan = L.new_workspace(db, n, dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev):
+        L.lora_plan_build(db, n, plan)
+        if ev: ev[0].record()
+        for shape, table, aligned, _, _, _ in launches:
+            L.lora_apply_multi(shape, db, plan, table, aligned)
+        if ev: ev[1].record()
+
+    wall, k_ms, _ = Timer(steps).run(step, warmup)
+    touched, slot_tokens, distinct = accounting.batch_work(batch.seg_bounds(), batch.idx, n)
+    byts = flops = 0
+    for _, _, _, probs, d_in, d_out in launches:
+        byts += len(probs) * accounting.call_bytes(touched, distinct, r, d_in, d_out, 2)
+        flops += len(probs) * accounting.lora_flops(slot_tokens, r, d_in, d_out)
+    return result("llama3-8b stack 32x7 mixed", wall, steps, touched, byts, flops, k_ms, byts, flops, len(launches),
+                  {"distinct_adapters": distinct, "note": "apply_* covers the 4 multi-problem launches together"})
+
+
+# -------------------------------------------------------------- cpu baseline --
+def cpu_baseline_decode(state, layers_sample=8, repeats=4):
+    """The fp64 oracle on the host for the headline workload: `layers_sample`
+    layers of one batch (only the adapters the batch touches are copied to the
+    host; the oracle's work does not depend on the others), repeated, scaled to
+    tokens/s through 32 layers."""
+    import oracle
+    torch = torch_mod()
+    pools, batches, xs, ys = state
+    b = batches[0]
+    used = np.unique(b.idx)
+    remap = {int(a): i for i, a in enumerate(used)}
+    idx = np.vectorize(lambda a: remap[int(a)])(b.idx).astype(np.int32)
+    host = []
+    for li in range(layers_sample):
+        A, B = pools[li]
+        sel = torch.from_numpy(used.astype(np.int64)).to(A.device)
+        host.append((A.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16),
+                     B.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16),
+                     xs[li].view(torch.int16).cpu().numpy().view(np.uint16),
+                     ys[li].view(torch.int16).cpu().numpy().view(np.uint16)))
+    orc = oracle.load()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        for A, B, x, y in host:
+            orc.apply(W.BF16, A, B, x, y, T=64, S=64, K=1, seg_off=None, idx=idx, nthreads=cores)
+    dt = time.perf_counter() - t0
+    per_layer = dt / (repeats * layers_sample)
+    return {"value": 64 / (per_layer * 32), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{layers_sample} of 32 layers x {repeats} repeats of one 64-token batch "
+                      f"({dt:.1f} s wall), scaled to 32 layers"}
+
+
+# --------------------------------------------------------------------- main --
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU only; requests would shard across GPUs "
+                                   "with no exchange, and no multi-GPU path is implemented",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    L.lib()
+    dev = "cuda:0"
+    only = set(s for s in args.only.split(",") if s)
+    want = lambda k: not only or k in only  # noqa: E731
+
+    variants = {}
+    head = state = None
+    if want("decode32"):
+        log("decode32 ...")
+        head, state = bench_decode_layers(dev, args.steps, args.warmup)
+    if want("c1"):
+        log("c1 ...")
+        variants["C1_tiny_fp32"] = bench_single(W.case_c1(), dev, args.steps, args.warmup, "C1 tiny fp32")
+    if want("c2"):
+        log("c2 ...")
+        variants["C2_decode_1layer"] = bench_single(W.case_c2(), dev, args.steps, args.warmup, "C2 decode q_proj 1 layer")
+    if want("c3"):
+        log("c3 ...")
+        variants["C3_prefill_r64"] = bench_single(W.case_c3(), dev, args.steps, args.warmup, "C3 prefill r64")
+    if want("c5"):
+        for d, r in [(1280, 64), (1280, 128), (640, 64), (640, 128)]:
+            log(f"c5 d{d} r{r} ...")
+            variants[f"C5_d{d}_r{r}"] = bench_single(W.case_c5(d, r), dev, args.steps, args.warmup,
+                                                     f"C5 diffusion d{d} r{r}")
+    if want("c4"):
+        log("c4 ...")
+        torch.cuda.empty_cache()
+        variants["C4_llama3_stack"] = bench_c4_stack(dev, max(5, args.steps // 5), max(2, args.warmup // 5))
+
+    cpu = None
+    if head is not None and not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        cpu = cpu_baseline_decode(state)
+
+    if head is None:  # a partial run: report the first variant as the line
+        name, head = next(iter(variants.items()))
+    line = {
+        "metric": "LoRA-delta tokens/s + achieved HBM GB/s (% of peak), decode & prefill SGMV",
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init adapters)",
+        "config": {"workload": head["workload"] + ": 64 requests x 1 token, Zipf(1.1) over 1000 resident rank-16 "
+                                                  "adapters per layer, 4096->4096 bf16, plan + one fused multi-layer "
+                                                  "launch per step", "global_batch": 64, "seq_len": 1,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": head["apply_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["apply_GBps"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "apply_kernel (fused shrink+expand)",
+                     "bytes_per_launch": head["apply_bytes_per_launch"], "avg_launch_us": head["apply_kernel_us"]},
+        "cpu_baseline": cpu,
+        "headline": head,
+        "variants": variants,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -17,6 +17,8 @@ struct Tune {
   int valu_max_chunks = 8;
   int mfma_items = 256;   // aim for about this many MFMA work items per launch
   int grid_cap = 2048;    // workgroups per launch; the kernels grid-stride over items
+  int decode = 0;         // fused vector-path VALU tiles run on the one-wave-per-item decode kernel
+  int decode_items = 4096;  // aim for about this many decode work items (waves) per launch
 };
 
 int env_int(const char *name, int dflt) {
@@ -32,6 +34,8 @@ const Tune &tune() {
     x.valu_max_chunks = env_int("LORA_VALU_MAX_CHUNKS", x.valu_max_chunks);
     x.mfma_items = env_int("LORA_MFMA_ITEMS", x.mfma_items);
     x.grid_cap = env_int("LORA_GRID_CAP", x.grid_cap);
+    x.decode = env_int("LORA_DECODE", x.decode);
+    x.decode_items = env_int("LORA_DECODE_ITEMS", x.decode_items);
     return x;
   }();
   return t;
@@ -106,12 +110,14 @@ int pow2_floor(int x) {
   return p;
 }
 
-// Choose the launch: vector path, MFMA eligibility, chunking, grid and LDS.
+// Choose the launches: vector path, MFMA eligibility, chunking, grids and LDS.
 struct Launch {
   bool vec;
-  int jt;
-  int grid;
-  size_t smem;
+  bool decode;      // VALU tiles on the decode kernel
+  bool valu;        // the VALU kernel runs
+  int jt;           // rank / 16 when the MFMA kernel runs, else 0
+  int grid_v, grid_m, grid_d;
+  size_t smem_v, smem_m, smem_d;
 };
 
 Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Plan &P, int n_problems, bool vec,
@@ -123,28 +129,52 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   const bool mfma = vec && shape->dtype == LORA_BF16 && (r == 16 || r == 32 || r == 64 || r == 128) &&
                     d.K * r <= kMfmaMaxSlotRank;
   L.jt = mfma ? r / 16 : 0;
+  a.valu_takes_m = mfma ? 0 : 1;
 
   // output-column chunks: more chunks per tile when there are few tiles
   const int est_v = std::max(1, std::min(d.S, shape->n_adapters)) * n_problems;
   const int est_m = std::max(1, (d.T + kMfmaRows - 1) / kMfmaRows) * n_problems;
+  L.decode = mode == MODE_FUSED && vec && tn.decode;
+  a.valu_skip_v = L.decode ? 1 : 0;
+  L.valu = !L.decode || a.valu_takes_m;
   int cv = 1, cm = 1;
   if (mode != MODE_SHRINK) {
-    cv = std::min(pow2_floor(std::max(1, tn.valu_items / est_v)), tn.valu_max_chunks);
+    const int want = L.decode ? tn.decode_items : tn.valu_items;
+    cv = std::min(pow2_floor(std::max(1, want / est_v)), tn.valu_max_chunks);
     cv = std::max(1, std::min(cv, std::max(1, d_out / 256)));
     cm = pow2_floor(std::max(1, tn.mfma_items / est_m));
     cm = std::max(1, std::min(cm, std::max(1, d_out / 512)));
   }
   a.wv = round_up((d_out + cv - 1) / cv, 64);
   a.cv = (d_out + a.wv - 1) / a.wv;
-  a.wm = round_up((d_out + cm - 1) / cm, 64);
+  a.wm = round_up((d_out + cm - 1) / cm, 128);
   a.cm = (d_out + a.wm - 1) / a.wm;
-  if (mode == MODE_SHRINK) { a.cv = a.cm = 1; a.wv = a.wm = round_up(d_out, 64); }
+  if (mode == MODE_SHRINK) { a.cv = a.cm = 1; a.wv = a.wm = round_up(d_out, 128); }
 
-  const int64_t max_items = (int64_t)n_problems * ((int64_t)P.L.bound_m * a.cm + (int64_t)P.L.bound_v * a.cv);
-  int64_t g = std::min<int64_t>(max_items, tn.grid_cap);
-  L.grid = round_up((int)std::max<int64_t>(g, 1), 8);
-  L.smem = apply_smem_bytes(r, a.kr_max, L.jt > 0);
+  const int64_t items_m = (int64_t)n_problems * P.L.bound_m * a.cm;
+  const int64_t tiles_v = (int64_t)n_problems * P.L.bound_v * a.cv;
+  const int64_t items_v = (L.decode ? 0 : tiles_v) + (a.valu_takes_m ? items_m : 0);
+  const int64_t groups_d = (tiles_v + kDecodeWaves - 1) / kDecodeWaves;
+  L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
+  L.grid_d = L.decode ? round_up((int)std::max<int64_t>(std::min<int64_t>(groups_d, tn.grid_cap), 1), 8) : 0;
+  L.smem_d = L.decode ? decode_smem_bytes(a.kr_max) : 0;
+  L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
+  L.smem_v = valu_smem_bytes(a.kr_max);
+  L.smem_m = mfma ? mfma_smem_bytes(L.jt, d.K) : 0;
   return L;
+}
+
+// MFMA tiles (the long groups) first, then the VALU tiles (decode kernel and/or VALU kernel).
+hipError_t launch_all(int mode, int dtype, const Launch &L, const ApplyArgs &a, hipStream_t stream) {
+  if (L.jt > 0) {
+    hipError_t e = launch_mfma(mode, L.jt, a, L.grid_m, L.smem_m, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (L.decode) {
+    hipError_t e = launch_decode(dtype, a, L.grid_d, L.smem_d, stream);
+    if (e != hipSuccess) return e;
+  }
+  return L.valu ? launch_valu(mode, dtype, L.vec, a, L.grid_v, L.smem_v, stream) : hipSuccess;
 }
 
 void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Plan &P, const lora_pool *shape) {
@@ -159,6 +189,7 @@ void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Pl
   a.cumlen = P.V.cumlen;
   a.tiles_m = P.V.tiles_m;
   a.tiles_v = P.V.tiles_v;
+  a.rowrec = P.V.rowrec;
   a.n = shape->n_adapters;
   a.r = shape->rank;
   a.d_in = shape->d_in;
@@ -194,7 +225,7 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
     return LORA_EINVAL;
 
   if (build) {
-    if (launch_plan(P.V, batch->seg_off, batch->idx, stream) != hipSuccess) return LORA_EHIP;
+    if (launch_plan(P.V, P.L.lds_bytes, batch->seg_off, batch->idx, stream) != hipSuccess) return LORA_EHIP;
   }
   if (d.T == 0 || d.S == 0) return LORA_OK;
 
@@ -218,7 +249,7 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
   a.v = v;
   a.ldv = ldv;
   const Launch L = configure(mode, pool, d, P, 1, vec, a);
-  if (launch_apply(mode, pool->dtype, L.vec, L.jt, a, L.grid, L.smem, stream) != hipSuccess) return LORA_EHIP;
+  if (launch_all(mode, pool->dtype, L, a, stream) != hipSuccess) return LORA_EHIP;
   return LORA_OK;
 }
 
@@ -254,7 +285,7 @@ lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *w
   if (n_adapters < 1) return LORA_ESHAPE;
   Plan P;
   if ((st = plan_for(d, n_adapters, ws, ws_bytes, P))) return st;
-  if (launch_plan(P.V, batch->seg_off, batch->idx, stream) != hipSuccess) return LORA_EHIP;
+  if (launch_plan(P.V, P.L.lds_bytes, batch->seg_off, batch->idx, stream) != hipSuccess) return LORA_EHIP;
   return LORA_OK;
 }
 
@@ -310,7 +341,7 @@ lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, co
   a.probs = problems;
   a.n_problems = n_problems;
   const Launch L = configure(MODE_FUSED, shape, d, P, n_problems, vec, a);
-  if (launch_apply(MODE_FUSED, shape->dtype, L.vec, L.jt, a, L.grid, L.smem, stream) != hipSuccess) return LORA_EHIP;
+  if (launch_all(MODE_FUSED, shape->dtype, L, a, stream) != hipSuccess) return LORA_EHIP;
   return LORA_OK;
 }
 

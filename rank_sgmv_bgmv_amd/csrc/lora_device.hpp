@@ -1,0 +1,326 @@
+// Device helpers shared by the VALU and MFMA apply kernels: bf16 numerics,
+// 16-byte vector element ops, the per-tile metadata kept in LDS, tile setup,
+// wave reductions and the work-item walk.
+#pragma once
+
+#include "lora_internal.hpp"
+
+namespace lora {
+
+// Global-memory accesses.  The tensors reach the kernels as plain pointers
+// (inside lora_problem), which the compiler cannot place in an address space;
+// it would emit FLAT instructions, which also count against the LDS counter so
+// every LDS access would wait for all loads in flight.  Every access to
+// caller memory goes through these, as a global (address space 1) access.
+#define LORA_GLOBAL __attribute__((address_space(1)))
+// raw register types of 2 .. 16 bytes (and 48 for a lora_problem)
+template <int N> struct Raw;
+template <> struct Raw<2> { typedef unsigned short type; };
+template <> struct Raw<4> { typedef unsigned int type; };
+template <> struct Raw<8> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
+template <> struct Raw<16> { typedef unsigned int type __attribute__((ext_vector_type(4))); };
+template <> struct Raw<48> {
+  struct type { Raw<16>::type q[3]; };
+};
+template <typename V, typename T>
+__device__ __forceinline__ V gload(const T *p) {
+  typedef typename Raw<sizeof(V)>::type R;
+  if constexpr (sizeof(V) == 48) {
+    const LORA_GLOBAL Raw<16>::type *q = (const LORA_GLOBAL Raw<16>::type *)(p);
+    R r;
+    r.q[0] = q[0]; r.q[1] = q[1]; r.q[2] = q[2];
+    return __builtin_bit_cast(V, r);
+  } else {
+    const R r = *(const LORA_GLOBAL R *)(p);
+    return __builtin_bit_cast(V, r);
+  }
+}
+template <typename V, typename T>
+__device__ __forceinline__ void gstore(T *p, const V &v) {
+  typedef typename Raw<sizeof(V)>::type R;
+  *(LORA_GLOBAL R *)(p) = __builtin_bit_cast(R, v);
+}
+
+// Access at a 32-bit byte offset from a wave-uniform base: one scalar base
+// register pair for many rows instead of one 64-bit address per row (the
+// global_load "saddr" form).  The offset must stay below 4 GiB.
+template <typename V, typename T>
+__device__ __forceinline__ V gload_at(const T *base, uint32_t byte_off) {
+  typedef typename Raw<sizeof(V)>::type R;
+  const R r = *(const LORA_GLOBAL R *)((const LORA_GLOBAL char *)base + byte_off);
+  return __builtin_bit_cast(V, r);
+}
+template <typename V, typename T>
+__device__ __forceinline__ void gstore_at(T *base, uint32_t byte_off, const V &v) {
+  typedef typename Raw<sizeof(V)>::type R;
+  *(LORA_GLOBAL R *)((LORA_GLOBAL char *)base + byte_off) = __builtin_bit_cast(R, v);
+}
+
+// A value every lane of the wave holds (read from LDS tile metadata): moved to
+// a scalar register, so address arithmetic on it stays scalar and loads use a
+// scalar base plus a 32-bit lane offset.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- numerics --
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf_to_f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round two floats to bf16 (round to nearest even, hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ uint16_t f_to_bf(float a) { return uint16_t(pack_bf2(a, 0.f) & 0xffffu); }
+
+__device__ __forceinline__ float dot2_bf(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// ----------------------------------------------------- element vector ops --
+// A "vector" is 16 bytes (8 bf16 / 4 fp32) on the vector path, one element otherwise.
+template <typename T, bool VEC> struct VOps;
+
+template <> struct VOps<uint16_t, true> {
+  static constexpr int E = 8;
+  typedef uint4 V;
+  static __device__ __forceinline__ V load(const uint16_t *p) { return gload<uint4>(p); }
+  static __device__ __forceinline__ V zero() { return make_uint4(0, 0, 0, 0); }
+  static __device__ __forceinline__ float dot(V a, V b, float acc) {
+    acc = dot2_bf(a.x, b.x, acc);
+    acc = dot2_bf(a.y, b.y, acc);
+    acc = dot2_bf(a.z, b.z, acc);
+    return dot2_bf(a.w, b.w, acc);
+  }
+  // sum_e v[e] * b[e], v in fp32
+  static __device__ __forceinline__ float dotf(const float *v, V b, float acc) {
+    const float4 v0 = *reinterpret_cast<const float4 *>(v);
+    const float4 v1 = *reinterpret_cast<const float4 *>(v + 4);
+    acc = fmaf(v0.x, bf_lo(b.x), acc); acc = fmaf(v0.y, bf_hi(b.x), acc);
+    acc = fmaf(v0.z, bf_lo(b.y), acc); acc = fmaf(v0.w, bf_hi(b.y), acc);
+    acc = fmaf(v1.x, bf_lo(b.z), acc); acc = fmaf(v1.y, bf_hi(b.z), acc);
+    acc = fmaf(v1.z, bf_lo(b.w), acc); acc = fmaf(v1.w, bf_hi(b.w), acc);
+    return acc;
+  }
+  static __device__ __forceinline__ void add_store(uint16_t *p, const float *d) {
+    uint4 y = load(p);
+    const float4 d0 = *reinterpret_cast<const float4 *>(d);
+    const float4 d1 = *reinterpret_cast<const float4 *>(d + 4);
+    uint4 o;
+    o.x = pack_bf2(bf_lo(y.x) + d0.x, bf_hi(y.x) + d0.y);
+    o.y = pack_bf2(bf_lo(y.y) + d0.z, bf_hi(y.y) + d0.w);
+    o.z = pack_bf2(bf_lo(y.z) + d1.x, bf_hi(y.z) + d1.y);
+    o.w = pack_bf2(bf_lo(y.w) + d1.z, bf_hi(y.w) + d1.w);
+    gstore(p, o);
+  }
+};
+
+template <> struct VOps<uint16_t, false> {
+  static constexpr int E = 1;
+  typedef uint16_t V;
+  static __device__ __forceinline__ V load(const uint16_t *p) { return gload<uint16_t>(p); }
+  static __device__ __forceinline__ V zero() { return 0; }
+  static __device__ __forceinline__ float dot(V a, V b, float acc) { return fmaf(bf_to_f(a), bf_to_f(b), acc); }
+  static __device__ __forceinline__ float dotf(const float *v, V b, float acc) { return fmaf(v[0], bf_to_f(b), acc); }
+  static __device__ __forceinline__ void add_store(uint16_t *p, const float *d) {
+    gstore(p, f_to_bf(bf_to_f(gload<uint16_t>(p)) + d[0]));
+  }
+};
+
+template <> struct VOps<float, true> {
+  static constexpr int E = 4;
+  typedef float4 V;
+  static __device__ __forceinline__ V load(const float *p) { return gload<float4>(p); }
+  static __device__ __forceinline__ V zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ __forceinline__ float dot(V a, V b, float acc) {
+    acc = fmaf(a.x, b.x, acc); acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc); return fmaf(a.w, b.w, acc);
+  }
+  static __device__ __forceinline__ float dotf(const float *v, V b, float acc) {
+    const float4 a = *reinterpret_cast<const float4 *>(v);
+    return dot(a, b, acc);
+  }
+  static __device__ __forceinline__ void add_store(float *p, const float *d) {
+    float4 y = load(p);
+    const float4 a = *reinterpret_cast<const float4 *>(d);
+    y.x += a.x; y.y += a.y; y.z += a.z; y.w += a.w;
+    gstore(p, y);
+  }
+};
+
+template <> struct VOps<float, false> {
+  static constexpr int E = 1;
+  typedef float V;
+  static __device__ __forceinline__ V load(const float *p) { return gload<float>(p); }
+  static __device__ __forceinline__ V zero() { return 0.f; }
+  static __device__ __forceinline__ float dot(V a, V b, float acc) { return fmaf(a, b, acc); }
+  static __device__ __forceinline__ float dotf(const float *v, V b, float acc) { return fmaf(v[0], b, acc); }
+  static __device__ __forceinline__ void add_store(float *p, const float *d) { gstore(p, gload<float>(p) + d[0]); }
+};
+
+// ------------------------------------------------------------ tile metadata --
+constexpr int kMetaRows = kMfmaRows;  // rows of tile metadata
+struct Meta {
+  int t[kMetaRows];                     // token row of each tile row
+  int a[LORA_MAX_SLOTS];                // the tile's adapters (compacted slot order)
+  int nact;                             // valid slots
+  int pad[3];
+  int pos[kMetaRows][LORA_MAX_SLOTS];   // original slot index of compacted slot
+  float sc[kMetaRows][LORA_MAX_SLOTS];  // scale of compacted slot
+  int cum[kMetaRows + 1];               // staging of the sorted row prefix sums (MFMA tiles)
+};
+constexpr size_t kMetaBytes = (sizeof(Meta) + 255) & ~size_t(255);
+
+// Fill the tile's rows (token index, compacted slots, scales) into LDS.  VALU
+// tiles carry one (token row, request) record per row; MFMA tiles find their
+// rows' requests by a binary search over the sorted rows' prefix sums, staged
+// in LDS with one parallel load.  Ends with a barrier.
+__device__ inline void setup_rows(const ApplyArgs &a, int4 td, const int2 *rec, int n_active, Meta &M) {
+  const int tid = threadIdx.x;
+  const int p0 = td.x, q0 = td.y, nrows = td.z;
+  if (!rec) {
+    // a tile's rows lie in requests q0 .. q0 + nrows - 1 (each holds >= 1 row)
+    const int nq = min(nrows, n_active - q0);
+    if (tid <= nq) M.cum[tid] = gload<int>(a.cumlen + q0 + tid);
+    __syncthreads();
+  }
+  if (tid < nrows) {
+    int s, t;
+    if (rec) {
+      const int2 rr = gload<int2>(rec + tid);
+      t = rr.x;
+      s = rr.y;
+    } else {
+      const int p = p0 + tid;
+      int lo = 0, hi = min(tid, n_active - 1 - q0);
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (M.cum[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      s = gload<int>(a.sseg + q0 + lo);
+      t = gload<int>(a.sst + q0 + lo) + (p - M.cum[lo]);
+    }
+    M.t[tid] = t;
+    int kk = 0;
+    for (int k = 0; k < a.K; ++k) {
+      const int ad = gload<int>(a.idx + (int64_t)s * a.K + k);
+      if (ad < 0 || ad >= a.n) continue;
+      M.pos[tid][kk] = k;
+      M.sc[tid][kk] = a.scale ? gload<float>(a.scale + (int64_t)s * a.K + k) : 1.0f;
+      if (tid == 0) M.a[kk] = ad;
+      ++kk;
+    }
+    if (tid == 0) M.nact = kk;
+  }
+  __syncthreads();
+}
+
+// Zero the intermediate columns of the empty slots of every row of a tile
+// (lora_shrink writes every column of a touched row).
+__device__ inline void zero_empty_slots(const ApplyArgs &a, int nrows, const Meta &M) {
+  for (int e = threadIdx.x; e < nrows * a.K; e += kThreads) {
+    const int m = e / a.K, k = e % a.K;
+    bool used = false;
+    for (int kk = 0; kk < M.nact; ++kk) used |= (M.pos[m][kk] == k);
+    if (!used) {
+      float *vp = a.v + (int64_t)M.t[m] * a.ldv + (int64_t)k * a.r;
+      for (int j = 0; j < a.r; ++j) gstore(vp + j, 0.f);
+    }
+  }
+}
+
+// Work items are (problem, tile, output chunk).  Every XCD takes a contiguous
+// range of items (blockIdx % 8 is the XCD a workgroup is dispatched to), so all
+// chunks of a tile and the neighbouring tiles of the same adapter share that
+// XCD's L2; the workgroups of an XCD stride through its range.
+template <class F>
+__device__ inline void walk_items(int64_t n_items, F &&body) {
+  if (n_items <= 0) return;
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+  const int64_t ipx = (n_items + 7) >> 3;
+  for (int64_t i = lb; i < ipx; i += per_xcd) {
+    const int64_t item = xcd * ipx + i;
+    if (item >= n_items) break;
+    body(item);
+    __syncthreads();
+  }
+}
+
+// Wave-wide sums of NV values per lane at once, as a butterfly
+// reduce-scatter: step S halves the values a lane holds, keeping the half
+// selected by lane bit S and adding the partner lane's copy of it.  After the
+// log2(NV) halving steps an all-reduce over the remaining lane bits finishes
+// the sum.  Lane l ends with the wave total of value (l % NV).
+template <int S, int NV>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[NV], int lane) {
+  const bool upper = (lane & S) != 0;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const float send = upper ? v[i] : v[i + S];
+    const float keep = upper ? v[i + S] : v[i];
+    v[i] = keep + __shfl_xor(send, S);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ float wave_sum_scatter(float (&v)[NV]) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (NV >= 64) reduce_scatter_step<32>(v, lane);
+  if constexpr (NV >= 32) reduce_scatter_step<16>(v, lane);
+  if constexpr (NV >= 16) reduce_scatter_step<8>(v, lane);
+  if constexpr (NV >= 8) reduce_scatter_step<4>(v, lane);
+  if constexpr (NV >= 4) reduce_scatter_step<2>(v, lane);
+  if constexpr (NV >= 2) reduce_scatter_step<1>(v, lane);
+  float s = v[0];
+#pragma unroll
+  for (int off = NV; off < 64; off <<= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+// y[0 .. RT) += acc, rounded once to T, with one vector access when aligned;
+// y is at byte offset `off` from p.
+template <typename T, bool VEC, int RT>
+__device__ __forceinline__ void add_store_rt(T *p, const float (&acc)[RT], uint32_t off = 0) {
+  if constexpr (VEC && sizeof(T) == 2 && RT == 8) {
+    uint4 y = gload_at<uint4>(p, off);
+    y.x = pack_bf2(bf_lo(y.x) + acc[0], bf_hi(y.x) + acc[1]);
+    y.y = pack_bf2(bf_lo(y.y) + acc[2], bf_hi(y.y) + acc[3]);
+    y.z = pack_bf2(bf_lo(y.z) + acc[4], bf_hi(y.z) + acc[5]);
+    y.w = pack_bf2(bf_lo(y.w) + acc[6], bf_hi(y.w) + acc[7]);
+    gstore_at(p, off, y);
+  } else if constexpr (VEC && sizeof(T) == 2 && RT == 4) {
+    uint2 y = gload_at<uint2>(p, off);
+    y.x = pack_bf2(bf_lo(y.x) + acc[0], bf_hi(y.x) + acc[1]);
+    y.y = pack_bf2(bf_lo(y.y) + acc[2], bf_hi(y.y) + acc[3]);
+    gstore_at(p, off, y);
+  } else if constexpr (VEC && sizeof(T) == 2 && RT == 2) {
+    const uint32_t y = gload_at<uint32_t>(p, off);
+    gstore_at(p, off, pack_bf2(bf_lo(y) + acc[0], bf_hi(y) + acc[1]));
+  } else if constexpr (VEC && sizeof(T) == 4 && RT >= 4) {
+#pragma unroll
+    for (int i = 0; i < RT; i += 4) {
+      float4 y = gload_at<float4>(p, off + 4 * i);
+      y.x += acc[i]; y.y += acc[i + 1]; y.z += acc[i + 2]; y.w += acc[i + 3];
+      gstore_at(p, off + 4 * i, y);
+    }
+  } else if constexpr (VEC && sizeof(T) == 4 && RT == 2) {
+    float2 y = gload_at<float2>(p, off);
+    y.x += acc[0]; y.y += acc[1];
+    gstore_at(p, off, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const uint32_t o = off + i * sizeof(T);
+      if constexpr (sizeof(T) == 2) gstore_at(p, o, f_to_bf(bf_to_f(gload_at<uint16_t>(p, o)) + acc[i]));
+      else gstore_at(p, o, gload_at<float>(p, o) + acc[i]);
+    }
+  }
+}
+
+}  // namespace lora

@@ -15,10 +15,10 @@ constexpr int kThreads = 256;       // apply kernels: 4 wave64s per workgroup
 constexpr int kMfmaRows = 64;       // rows per MFMA tile (16 per wave)
 constexpr int kValuRows = 16;       // rows per VALU tile
 constexpr int kMfmaMinRows = 17;    // adapter groups with at least this many rows get MFMA tiles
-constexpr int kRowBlock = 8;        // rows per VALU pass
-constexpr int kValuOutChunk = 512;  // outputs per VALU expand sub-chunk (LDS staging of the delta)
+constexpr int kRowBlock = 4;        // rows per VALU pass (register budget of the VALU tile body)
 constexpr int kMfmaMaxRank = 128;   // MFMA tiles serve ranks 16, 32, 64, 128
 constexpr int kMfmaMaxSlotRank = 512;
+constexpr int kMaxLdsBytes = 160 * 1024;  // LDS a gfx950 workgroup may allocate
 
 // Plan header words (int32).
 enum {
@@ -36,9 +36,13 @@ constexpr int kPlanMagic = 0x4c6f5241;  // "LoRA"
 
 // Byte offsets of the plan arrays inside the workspace.
 struct PlanLayout {
-  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, tiles_m, tiles_v, total;
+  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, tiles_m, tiles_v, rowrec, total;
   int S, T, n, bound_m, bound_v;
+  size_t lds_bytes;  // LDS the plan kernel uses for its working arrays (0: they stay in global memory)
 };
+
+// The plan kernel keeps its working arrays in LDS when they fit in this budget.
+constexpr size_t kPlanLdsBudget = 144 * 1024;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -63,7 +67,12 @@ inline PlanLayout plan_layout(int S, int T, int n) {
   L.toff_v = take(sizeof(int) * (size_t(S) + 2));
   L.tiles_m = take(sizeof(int4) * size_t(L.bound_m));
   L.tiles_v = take(sizeof(int4) * size_t(L.bound_v));
+  L.rowrec = take(sizeof(int2) * kValuRows * size_t(L.bound_v));
   L.total = off;
+  // working arrays: start, key, sseg, sst (S+1 each), cumlen, gtmp, gstart, toff_m, toff_v (S+2 each),
+  // cnt, cur (n+2 each)
+  const size_t lds_ints = 4 * (size_t(S) + 1) + 5 * (size_t(S) + 2) + 2 * (size_t(n) + 2);
+  L.lds_bytes = lds_ints * sizeof(int) <= kPlanLdsBudget ? lds_ints * sizeof(int) : 0;
   return L;
 }
 
@@ -71,7 +80,9 @@ inline PlanLayout plan_layout(int S, int T, int n) {
 struct PlanView {
   int *hdr, *start, *key, *cnt, *cur, *sseg, *sst, *cumlen, *gtmp, *gstart, *toff_m, *toff_v;
   int4 *tiles_m, *tiles_v;
+  int2 *rowrec;  // per VALU tile: (token row, request) of each of its rows
   int S, T, n, K, per_token;
+  int lds_mode;
 };
 
 inline PlanView plan_view(void *ws, const PlanLayout &L, int K, int per_token) {
@@ -91,7 +102,9 @@ inline PlanView plan_view(void *ws, const PlanLayout &L, int K, int per_token) {
   P.toff_v = reinterpret_cast<int *>(b + L.toff_v);
   P.tiles_m = reinterpret_cast<int4 *>(b + L.tiles_m);
   P.tiles_v = reinterpret_cast<int4 *>(b + L.tiles_v);
+  P.rowrec = reinterpret_cast<int2 *>(b + L.rowrec);
   P.S = L.S; P.T = L.T; P.n = L.n; P.K = K; P.per_token = per_token;
+  P.lds_mode = L.lds_bytes > 0;
   return P;
 }
 
@@ -106,6 +119,7 @@ struct ApplyArgs {
   // plan (read only)
   const int *hdr, *sseg, *sst, *cumlen;
   const int4 *tiles_m, *tiles_v;
+  const int2 *rowrec;
   // shape shared by every problem
   int n, r, d_in, d_out;
   // problems
@@ -119,14 +133,23 @@ struct ApplyArgs {
   int64_t ldv;
   // layout of dynamic LDS
   int kr_max;      // max_slots * rank (row stride of the VALU intermediate)
+  int valu_takes_m;  // the VALU kernel also runs the MFMA-sized tiles (no MFMA kernel launched)
+  int valu_skip_v;   // the VALU kernel leaves the VALU tiles to the decode kernel
 };
 
-size_t apply_smem_bytes(int r, int kr_max, bool mfma);
+size_t valu_smem_bytes(int kr_max);
+size_t decode_smem_bytes(int kr_max);
+size_t mfma_smem_bytes(int jt, int slots);
 
-hipError_t launch_plan(const PlanView &P, const int *seg_off, const int *idx, hipStream_t stream);
+hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, const int *idx, hipStream_t stream);
 
-// dtype: LORA_F32 / LORA_BF16; vec: 16-byte vector path; jt: rank/16 for MFMA tiles (0 = no MFMA).
-hipError_t launch_apply(int mode, int dtype, bool vec, int jt, const ApplyArgs &args, int grid, size_t smem,
-                        hipStream_t stream);
+// VALU kernel: dtype LORA_F32 / LORA_BF16, vec = 16-byte vector path.
+hipError_t launch_valu(int mode, int dtype, bool vec, const ApplyArgs &args, int grid, size_t smem,
+                       hipStream_t stream);
+// Decode kernel (fused mode, vector path): one wave per VALU-tile work item.
+constexpr int kDecodeWaves = kThreads / 64;
+hipError_t launch_decode(int dtype, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
+// MFMA kernel (bf16, vector path): jt = rank / 16 in {1, 2, 4, 8}.
+hipError_t launch_mfma(int mode, int jt, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
 
 }  // namespace lora

@@ -1,0 +1,303 @@
+// MFMA apply kernel: prefill tiles of 64 rows of one adapter group, bf16,
+// rank 16 / 32 / 64 / 128.  Computes y += scale * (x A_i^T) B_i^T for the
+// tile's rows with both contractions on the matrix cores.
+//
+// "Serving several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
+// alongside": the unmerged form adds x A^T B^T to x W^T; "Exercises" (four
+// requests): requests that share a LoRA fall into one group, "making the matrix
+// multiply larger and more efficient" -- the long groups are the ones dense
+// enough for MFMA.  Comparison table, "Stacking several LoRAs": stacked
+// adapters are summed; here the slots of a tile share one accumulator.
+//
+// Layout of the work.  Wave w owns tile rows 16w .. 16w+15.
+//   Shrink (per slot): V^T[j][t] = sum_c A[j][c] x[t][c] on
+//     v_mfma_f32_16x16x32_bf16.  d_in is walked in stages of KC columns.  A
+//     (L2-resident: every tile of the group reads it) is staged through LDS,
+//     shared by the four waves, with the next stage prefetched into
+//     registers; x (the HBM stream) goes straight into MFMA operand registers,
+//     one stage ahead, double buffered.  Two barriers per stage.
+//     The accumulator layout gives lane (t, q) the values v[t][16 jt + 4q ..
+//     +3]; scaled and rounded once to bf16 they are exactly the B operand of
+//     the expand's v_mfma_f32_16x16x16_bf16.  Each lane parks them in LDS
+//     (its own row, read back only by itself) until the expand.
+//   Expand: Y^T[o][t] += sum_j B[o][j] v[t][j] per stage of 128 outputs (and
+//     per slot).  B is staged through LDS with the next stage prefetched into
+//     registers; y is read one stage ahead straight into the accumulator
+//     layout (8-byte pieces: lane (t, q) holds y[t][o + 4q .. +3]), added
+//     and rounded once to bf16, and written back.
+// Every bf16 product is exact in fp32 and accumulation is fp32; the rank-r
+// intermediate is rounded once to bf16 before the expand.
+
+#include "lora_device.hpp"
+
+namespace lora {
+namespace {
+
+__device__ __forceinline__ f32x4 mfma32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                    0, 0);
+}
+
+template <int JT>
+struct MfmaCfg {
+  static constexpr int R = 16 * JT;
+  static constexpr int KC = R <= 64 ? 256 : 128;           // d_in columns per shrink stage
+  static constexpr int KS = KC / 32;                       // k-steps per stage
+  static constexpr int AST = KC + 8;                       // staged A row stride (elements)
+  static constexpr int NAV = R * (KC / 8) / kThreads;      // 16-byte A pieces per thread per stage
+  static constexpr int NO = 128;                           // outputs per expand stage
+  static constexpr int OT = NO / 16;                       // 16-wide output tiles per stage
+  static constexpr int BST = R + 8;                        // staged B row stride (elements)
+  static constexpr int NBV = NO * (R / 8) / kThreads;      // 16-byte B pieces per thread per stage
+  static constexpr size_t LDS = (size_t(R) * AST > size_t(NO) * BST ? size_t(R) * AST : size_t(NO) * BST) * 2;
+  static constexpr int VST = R + 8;                        // row stride (elements) of the parked intermediate
+  static_assert(NAV >= 1 && NBV >= 1, "stage sizes");
+};
+
+template <int JT, int MODE>
+__device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, const Meta &M,
+                          uint16_t *stage, uint16_t *vpark) {
+  typedef MfmaCfg<JT> C;
+  constexpr int R = C::R, KC = C::KC, KS = C::KS, AST = C::AST, NAV = C::NAV;
+  constexpr int NO = C::NO, OT = C::OT, BST = C::BST, NBV = C::NBV, VST = C::VST;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int m = 16 * w + l16;  // this lane's tile row
+  const bool row_ok = m < nrows;
+  const bool wave_live = 16 * w < nrows;
+  const int d_in = a.d_in, d_out = a.d_out, nact = M.nact;
+  const int64_t trow = M.t[row_ok ? m : 0];
+  const uint16_t *__restrict__ xrow = static_cast<const uint16_t *>(pr.x) + trow * pr.ldx;
+  uint16_t *__restrict__ yrow = static_cast<uint16_t *>(pr.y) + trow * pr.ldy;
+
+  // parked bf16 intermediate of this lane: v[t][16 jt + 4 kg .. +3] of compacted slot kk
+  auto vslot = [&](int kk, int jt) -> uint2 * {
+    return reinterpret_cast<uint2 *>(vpark + ((int64_t)kk * kMfmaRows + m) * VST + 16 * jt + 4 * kg);
+  };
+
+  // ------------------------------------------------------------ shrink --
+  for (int kk = 0; kk < nact; ++kk) {
+    if (MODE == MODE_EXPAND) {
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row_ok)
+          f = gload<float4>(a.v + trow * a.ldv + (int64_t)M.pos[m][kk] * R + 16 * jt + 4 * kg);
+        *vslot(kk, jt) = make_uint2(pack_bf2(f.x, f.y), pack_bf2(f.z, f.w));
+      }
+      continue;
+    }
+    const uint16_t *__restrict__ Aa = static_cast<const uint16_t *>(pr.A) + (int64_t)M.a[kk] * R * d_in;
+    f32x4 acc[JT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 ar[NAV];      // next A stage (cooperative, all threads)
+    uint4 x0[KS], x1[KS];  // x operands of the current / next stage (this lane's row)
+
+    auto load_a = [&](int kc) {
+#pragma unroll
+      for (int i = 0; i < NAV; ++i) {
+        const int e = tid + i * kThreads;
+        const int row = e / (KC / 8), c = kc + 8 * (e % (KC / 8));
+        ar[i] = c < d_in ? gload<uint4>(Aa + (int64_t)row * d_in + c) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto load_x = [&](int kc, uint4(&xr)[KS]) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = kc + 32 * ks + 8 * kg;
+        xr[ks] = (row_ok && c < d_in) ? gload<uint4>(xrow + c) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    // one stage: publish the A stage held in `ar`, prefetch the next, multiply
+    auto step = [&](int kc, const uint4(&xc)[KS], uint4(&xn)[KS]) {
+      __syncthreads();  // every wave is done reading the previous stage
+#pragma unroll
+      for (int i = 0; i < NAV; ++i) {
+        const int e = tid + i * kThreads;
+        *reinterpret_cast<uint4 *>(stage + (e / (KC / 8)) * AST + 8 * (e % (KC / 8))) = ar[i];
+      }
+      __syncthreads();
+      if (kc + KC < d_in) {
+        load_a(kc + KC);
+        load_x(kc + KC, xn);
+      }
+      if (wave_live) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt) {
+            const uint4 av = *reinterpret_cast<const uint4 *>(stage + (16 * jt + l16) * AST + 32 * ks + 8 * kg);
+            acc[jt] = mfma32(av, xc[ks], acc[jt]);
+          }
+        }
+      }
+    };
+    load_a(0);
+    load_x(0, x0);
+    for (int kc = 0; kc < d_in; kc += 2 * KC) {
+      step(kc, x0, x1);
+      if (kc + KC < d_in) step(kc + KC, x1, x0);
+    }
+    // acc[jt][q] = v[t_m][16 jt + 4 kg + q], unscaled
+    const float sc = row_ok ? M.sc[m][kk] : 0.f;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const f32x4 s = acc[jt] * sc;
+      if (MODE == MODE_SHRINK) {
+        if (row_ok)
+          gstore(a.v + trow * a.ldv + (int64_t)M.pos[m][kk] * R + 16 * jt + 4 * kg, make_float4(s[0], s[1], s[2], s[3]));
+      } else {
+        *vslot(kk, jt) = make_uint2(pack_bf2(s[0], s[1]), pack_bf2(s[2], s[3]));
+      }
+    }
+  }
+  if (MODE == MODE_SHRINK) {
+    zero_empty_slots(a, nrows, M);
+    return;
+  }
+
+  // ------------------------------------------------------------ expand --
+  // stages are (output block ob, slot kk), slot-minor
+  const int n_ob = (o_hi - o_lo + NO - 1) / NO;
+  const int n_st = n_ob * nact;
+  uint4 br[NBV];                 // next B stage (cooperative)
+  uint2 yc[OT], yn[OT];          // y pieces of the current / next output block
+  f32x4 yacc[OT];
+  auto load_b = [&](int st) {
+    const int ob = o_lo + (st / nact) * NO, kk = st % nact;
+    const uint16_t *__restrict__ Bk = static_cast<const uint16_t *>(pr.B) + (int64_t)M.a[kk] * d_out * R;
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / (R / 8), c = 8 * (e % (R / 8));
+      br[i] = ob + row < o_hi ? gload<uint4>(Bk + (int64_t)(ob + row) * R + c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto load_y = [&](int ob, uint2(&yr)[OT]) {
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) {
+      const int o = ob + 16 * ot + 4 * kg;
+      yr[ot] = (row_ok && o < o_hi) ? gload<uint2>(yrow + o) : make_uint2(0, 0);
+    }
+  };
+  if (n_st > 0) {
+    load_b(0);
+    load_y(o_lo, yc);
+  }
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < n_st; ++st) {
+    const int ob = o_lo + (st / nact) * NO, kk = st % nact;
+    __syncthreads();  // every wave is done reading the previous stage
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) {
+      const int e = tid + i * kThreads;
+      *reinterpret_cast<uint4 *>(stage + (e / (R / 8)) * BST + 8 * (e % (R / 8))) = br[i];
+    }
+    __syncthreads();
+    if (st + 1 < n_st) {
+      load_b(st + 1);
+      if ((st + 1) % nact == 0) load_y(ob + NO, yn);
+    }
+    if (wave_live) {
+      uint2 v[JT];
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) v[jt] = *vslot(kk, jt);
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
+          yacc[ot] = mfma16(bv, v[jt], yacc[ot]);
+        }
+      }
+    }
+    if (kk == nact - 1) {
+      // output block done: y += delta, rounded once, written back
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) {
+        const int o = ob + 16 * ot + 4 * kg;
+        if (row_ok && o < o_hi) {
+          const uint2 y0 = yc[ot];
+          gstore(yrow + o, make_uint2(pack_bf2(bf_lo(y0.x) + yacc[ot][0], bf_hi(y0.x) + yacc[ot][1]),
+                                      pack_bf2(bf_lo(y0.y) + yacc[ot][2], bf_hi(y0.y) + yacc[ot][3])));
+        }
+        yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
+        yc[ot] = yn[ot];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernel --
+template <int JT, int MODE>
+__global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  Meta &M = *reinterpret_cast<Meta *>(smem);
+  uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
+  uint16_t *vpark = reinterpret_cast<uint16_t *>(smem + kMetaBytes + MfmaCfg<JT>::LDS);
+  const int n_m = gload<int>(a.hdr + H_TILES_M), n_active = gload<int>(a.hdr + H_ACTIVE);
+  const int64_t per_prob = (int64_t)n_m * a.cm;
+  walk_items(per_prob * a.n_problems, [&](int64_t item) {
+    const int p = int(item / per_prob);
+    const int64_t rem = item - (int64_t)p * per_prob;
+    const int tile = int(rem / a.cm), chunk = int(rem % a.cm);
+    const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
+    const int4 td = gload<int4>(a.tiles_m + tile);
+    const int o_lo = chunk * a.wm, o_hi = min(a.d_out, o_lo + a.wm);
+    setup_rows(a, td, nullptr, n_active, M);
+    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) mfma_tile<JT, MODE>(a, pr, td.z, o_lo, o_hi, M, stage, vpark);
+  });
+}
+
+// Launch one instantiation; the first launch lifts its dynamic-LDS limit to
+// the 160 KB a gfx950 workgroup may use.
+template <int JT, int M>
+hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  static const bool lds_limit_raised =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_kernel<JT, M>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+  (void)lds_limit_raised;
+  hipLaunchKernelGGL((mfma_kernel<JT, M>), dim3(grid), dim3(kThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int JT>
+hipError_t launch_jt(int mode, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  switch (mode) {
+    case MODE_FUSED: return launch_one<JT, MODE_FUSED>(a, grid, smem, stream);
+    case MODE_SHRINK: return launch_one<JT, MODE_SHRINK>(a, grid, smem, stream);
+    case MODE_EXPAND: return launch_one<JT, MODE_EXPAND>(a, grid, smem, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Meta + staging + the parked intermediate of up to `slots` slots.
+size_t mfma_smem_bytes(int jt, int slots) {
+  switch (jt) {
+    case 1: return kMetaBytes + MfmaCfg<1>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<1>::VST * 2;
+    case 2: return kMetaBytes + MfmaCfg<2>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<2>::VST * 2;
+    case 4: return kMetaBytes + MfmaCfg<4>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<4>::VST * 2;
+    case 8: return kMetaBytes + MfmaCfg<8>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<8>::VST * 2;
+  }
+  return 0;
+}
+
+hipError_t launch_mfma(int mode, int jt, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  switch (jt) {
+    case 1: return launch_jt<1>(mode, a, grid, smem, stream);
+    case 2: return launch_jt<2>(mode, a, grid, smem, stream);
+    case 4: return launch_jt<4>(mode, a, grid, smem, stream);
+    case 8: return launch_jt<8>(mode, a, grid, smem, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lora

@@ -19,7 +19,9 @@
 //   4. prefix sums of the sorted requests' lengths (rows in sorted order);
 //   5. group boundaries; a group of >= kMfmaMinRows rows is cut into MFMA
 //      tiles of kMfmaRows rows, a smaller one into VALU tiles of kValuRows;
-//   6. one tile descriptor per tile: {first row, first request, rows, group end}.
+//   6. one tile descriptor per tile: {first row, first request, rows, group end},
+//      and for VALU tiles one (token row, request) record per row, so the
+//      apply kernel starts streaming after two dependent loads.
 // Rows never move: a tile names rows by (sorted request, offset) and the apply
 // kernels read and write x / y rows in place.
 
@@ -87,7 +89,9 @@ __device__ int block_incl_scan_max(int v, int *sh, int &total) {
   return res;
 }
 
-// out[i] = sum_{j<i} in[i]; in and out may alias.  Returns the total.
+// out[i] = sum_{j<i} in[j]; in and out may alias.  Returns the total.  Thread
+// i % 1024 writes out[i] after the scan's last barrier: other threads may read
+// it only after a further __syncthreads().
 __device__ int chunked_excl_scan(const int *in, int *out, int N, int *sh) {
   int carry = 0;
   for (int base = 0; base < N; base += kPlanThreads) {
@@ -112,18 +116,37 @@ __device__ __forceinline__ int last_le(const int *a, int lo, int hi, int key) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const int *__restrict__ seg_off,
                                                             const int *__restrict__ idx) {
+  extern __shared__ int lds[];
   __shared__ int sh[20];
   __shared__ int s_err;
   const int tid = threadIdx.x;
   const int S = P.S, T = P.T, n = P.n, K = P.K;
 
+  // Working arrays: in LDS when they fit (small batches: no global round trips
+  // between the phases), else in the workspace.  Flat pointers serve both.
+  int *start = P.start, *key = P.key, *cnt = P.cnt, *cur = P.cur, *sseg = P.sseg, *sst = P.sst,
+      *cumlen = P.cumlen, *gtmp = P.gtmp, *gstart = P.gstart, *toff_m = P.toff_m, *toff_v = P.toff_v;
+  if (P.lds_mode) {
+    int *q = lds;
+    start = q; q += S + 1;
+    key = q; q += S + 1;
+    sseg = q; q += S + 1;
+    sst = q; q += S + 1;
+    cumlen = q; q += S + 2;
+    gtmp = q; q += S + 2;
+    gstart = q; q += S + 2;
+    toff_m = q; q += S + 2;
+    toff_v = q; q += S + 2;
+    cnt = q; q += n + 2;
+    cur = q;
+  }
+
   if (tid == 0) s_err = 0;
-  for (int b = tid; b <= n; b += kPlanThreads) P.cnt[b] = 0;
-  __syncthreads();
+  for (int b = tid; b <= n; b += kPlanThreads) cnt[b] = 0;
 
   // 1. sanitised request starts, start[S] = end of the last request.
   if (P.per_token) {
-    for (int s = tid; s <= S; s += kPlanThreads) P.start[s] = s;
+    for (int s = tid; s <= S; s += kPlanThreads) start[s] = s;
   } else {
     int carry = 0;
     for (int base = 0; base <= S; base += kPlanThreads) {
@@ -139,7 +162,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
       }
       int tot;
       const int m = block_incl_scan_max(v, sh, tot);
-      if (s <= S) P.start[s] = min(max(max(m, carry), 0), T);
+      if (s <= S) start[s] = min(max(max(m, carry), 0), T);
       carry = max(carry, tot);
     }
   }
@@ -147,7 +170,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
 
   // 2. keys and histogram.
   for (int s = tid; s < S; s += kPlanThreads) {
-    const int len = P.start[s + 1] - P.start[s];
+    const int len = start[s + 1] - start[s];
     int nact = 0, a0 = -1;
     for (int k = 0; k < K; ++k) {
       const int a = idx[(int64_t)s * K + k];
@@ -156,76 +179,90 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
       if (nact == 0) a0 = a;
       ++nact;
     }
-    const int key = (len <= 0 || nact == 0) ? -1 : (nact == 1 ? a0 : n);
-    P.key[s] = key;
-    if (key >= 0) atomicAdd(&P.cnt[key], 1);
+    const int kk = (len <= 0 || nact == 0) ? -1 : (nact == 1 ? a0 : n);
+    key[s] = kk;
+    if (kk >= 0) atomicAdd(&cnt[kk], 1);
   }
   __syncthreads();
 
   // 3. bucket starts, then scatter (order inside a bucket is not significant).
-  const int n_active = chunked_excl_scan(P.cnt, P.cur, n + 1, sh);
-  __syncthreads();
+  const int n_active = chunked_excl_scan(cnt, cur, n + 1, sh);
+  __syncthreads();  // the scan writes its output after its last barrier
   for (int s = tid; s < S; s += kPlanThreads) {
-    const int key = P.key[s];
-    if (key >= 0) P.sseg[atomicAdd(&P.cur[key], 1)] = s;
+    const int kk = key[s];
+    if (kk >= 0) sseg[atomicAdd(&cur[kk], 1)] = s;
   }
   __syncthreads();
 
-  // 4. rows in sorted order.
+  // 4. rows in sorted order; group-start flags (a group starts where the key
+  //    changes; every multi-adapter request is its own group).
   for (int q = tid; q < n_active; q += kPlanThreads) {
-    const int s = P.sseg[q];
-    P.sst[q] = P.start[s];
-    P.cumlen[q] = P.start[s + 1] - P.start[s];
+    const int s = sseg[q];
+    sst[q] = start[s];
+    cumlen[q] = start[s + 1] - start[s];
+    const int kq = key[s];
+    gtmp[q] = (q == 0 || kq == n || kq != key[sseg[q - 1]]) ? 1 : 0;
   }
   __syncthreads();
-  const int total_rows = chunked_excl_scan(P.cumlen, P.cumlen, n_active, sh);
-  if (tid == 0) P.cumlen[n_active] = total_rows;
+  const int total_rows = chunked_excl_scan(cumlen, cumlen, n_active, sh);
+  if (tid == 0) cumlen[n_active] = total_rows;
+  // 5. group starts: compact the flags (the flag of q is gtmp[q+1] - gtmp[q] after the scan)
+  for (int q = tid; q < n_active; q += kPlanThreads) gstart[q] = gtmp[q];
   __syncthreads();
-
-  // 5. groups: a new group starts where the key changes; every multi-adapter request is its own group.
-  for (int q = tid; q < n_active; q += kPlanThreads) {
-    const int kq = P.key[P.sseg[q]];
-    P.gtmp[q] = (q == 0 || kq == n || kq != P.key[P.sseg[q - 1]]) ? 1 : 0;
-  }
-  __syncthreads();
-  for (int q = tid; q < n_active; q += kPlanThreads) P.gstart[q] = P.gtmp[q];  // keep flags
-  __syncthreads();
-  const int n_groups = chunked_excl_scan(P.gtmp, P.gtmp, n_active, sh);
-  __syncthreads();
-  // gstart currently holds the flags; write starts into toff_m temporarily, then copy.
+  const int n_groups = chunked_excl_scan(gtmp, gtmp, n_active, sh);
   for (int q = tid; q < n_active; q += kPlanThreads)
-    if (P.gstart[q]) P.toff_m[P.gtmp[q]] = q;
+    if (gstart[q]) toff_m[gtmp[q]] = q;
   __syncthreads();
-  for (int g = tid; g < n_groups; g += kPlanThreads) P.gstart[g] = P.toff_m[g];
-  if (tid == 0) P.gstart[n_groups] = n_active;
+  for (int g = tid; g < n_groups; g += kPlanThreads) gstart[g] = toff_m[g];
+  if (tid == 0) gstart[n_groups] = n_active;
   __syncthreads();
 
   // tiles per group
   for (int g = tid; g < n_groups; g += kPlanThreads) {
-    const int rows = P.cumlen[P.gstart[g + 1]] - P.cumlen[P.gstart[g]];
+    const int rows = cumlen[gstart[g + 1]] - cumlen[gstart[g]];
     const bool big = rows >= kMfmaMinRows;
-    P.toff_m[g] = big ? (rows + kMfmaRows - 1) / kMfmaRows : 0;
-    P.toff_v[g] = big ? 0 : (rows + kValuRows - 1) / kValuRows;
+    toff_m[g] = big ? (rows + kMfmaRows - 1) / kMfmaRows : 0;
+    toff_v[g] = big ? 0 : (rows + kValuRows - 1) / kValuRows;
   }
   __syncthreads();
-  const int nt_m = chunked_excl_scan(P.toff_m, P.toff_m, n_groups, sh);
-  const int nt_v = chunked_excl_scan(P.toff_v, P.toff_v, n_groups, sh);
-  if (tid == 0) { P.toff_m[n_groups] = nt_m; P.toff_v[n_groups] = nt_v; }
+  const int nt_m = chunked_excl_scan(toff_m, toff_m, n_groups, sh);
+  const int nt_v = chunked_excl_scan(toff_v, toff_v, n_groups, sh);
+  if (tid == 0) { toff_m[n_groups] = nt_m; toff_v[n_groups] = nt_v; }
   __syncthreads();
 
-  // 6. tile descriptors
+  // 6. tile descriptors; VALU tiles also get one (token row, request) record per row
   for (int u = tid; u < nt_m + nt_v; u += kPlanThreads) {
     const bool is_m = u < nt_m;
     const int uu = is_m ? u : u - nt_m;
-    const int *toff = is_m ? P.toff_m : P.toff_v;
+    const int *toff = is_m ? toff_m : toff_v;
     const int rows_per = is_m ? kMfmaRows : kValuRows;
     const int g = last_le(toff, 0, n_groups - 1, uu);
-    const int gs = P.gstart[g], ge = P.gstart[g + 1];
-    const int p0 = P.cumlen[gs] + (uu - toff[g]) * rows_per;
-    const int nrows = min(rows_per, P.cumlen[ge] - p0);
-    const int q0 = last_le(P.cumlen, gs, ge - 1, p0);
+    const int gs = gstart[g], ge = gstart[g + 1];
+    const int p0 = cumlen[gs] + (uu - toff[g]) * rows_per;
+    const int nrows = min(rows_per, cumlen[ge] - p0);
+    const int q0 = last_le(cumlen, gs, ge - 1, p0);
     const int4 d = make_int4(p0, q0, nrows, ge);
-    if (is_m) P.tiles_m[uu] = d; else P.tiles_v[uu] = d;
+    if (is_m) {
+      P.tiles_m[uu] = d;
+    } else {
+      P.tiles_v[uu] = d;
+      int q = q0;
+      for (int i = 0; i < nrows; ++i) {
+        const int p = p0 + i;
+        while (cumlen[q + 1] <= p) ++q;
+        P.rowrec[(int64_t)uu * kValuRows + i] = make_int2(sst[q] + (p - cumlen[q]), sseg[q]);
+      }
+    }
+  }
+
+  // the apply kernels read these three arrays for MFMA tiles
+  if (P.lds_mode) {
+    for (int q = tid; q < n_active; q += kPlanThreads) {
+      P.sseg[q] = sseg[q];
+      P.sst[q] = sst[q];
+      P.cumlen[q] = cumlen[q];
+    }
+    if (tid == 0) P.cumlen[n_active] = total_rows;
   }
 
   __syncthreads();
@@ -246,8 +283,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
 
 }  // namespace
 
-hipError_t launch_plan(const PlanView &P, const int *seg_off, const int *idx, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, P, seg_off, idx);
+hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, const int *idx, hipStream_t stream) {
+  static const bool lds_limit_raised =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(plan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          int(kPlanLdsBudget)) == hipSuccess;
+  (void)lds_limit_raised;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), P.lds_mode ? lds_bytes : 0, stream, P, seg_off, idx);
   return hipGetLastError();
 }
 
