@@ -17,8 +17,6 @@ struct Tune {
   int valu_max_chunks = 8;
   int mfma_items = 256;   // aim for about this many MFMA work items per launch
   int grid_cap = 2048;    // workgroups per launch; the kernels grid-stride over items
-  int decode = 0;         // fused vector-path VALU tiles run on the one-wave-per-item decode kernel
-  int decode_items = 4096;  // aim for about this many decode work items (waves) per launch
 };
 
 int env_int(const char *name, int dflt) {
@@ -34,8 +32,6 @@ const Tune &tune() {
     x.valu_max_chunks = env_int("LORA_VALU_MAX_CHUNKS", x.valu_max_chunks);
     x.mfma_items = env_int("LORA_MFMA_ITEMS", x.mfma_items);
     x.grid_cap = env_int("LORA_GRID_CAP", x.grid_cap);
-    x.decode = env_int("LORA_DECODE", x.decode);
-    x.decode_items = env_int("LORA_DECODE_ITEMS", x.decode_items);
     return x;
   }();
   return t;
@@ -113,11 +109,9 @@ int pow2_floor(int x) {
 // Choose the launches: vector path, MFMA eligibility, chunking, grids and LDS.
 struct Launch {
   bool vec;
-  bool decode;      // VALU tiles on the decode kernel
-  bool valu;        // the VALU kernel runs
   int jt;           // rank / 16 when the MFMA kernel runs, else 0
-  int grid_v, grid_m, grid_d;
-  size_t smem_v, smem_m, smem_d;
+  int grid_v, grid_m;
+  size_t smem_v, smem_m;
 };
 
 Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Plan &P, int n_problems, bool vec,
@@ -127,20 +121,16 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   Launch L;
   L.vec = vec;
   const bool mfma = vec && shape->dtype == LORA_BF16 && (r == 16 || r == 32 || r == 64 || r == 128) &&
-                    d.K * r <= kMfmaMaxSlotRank;
+                    d.K * r <= kMfmaMaxSlotRank && d.T >= kMfmaMinBatch;
   L.jt = mfma ? r / 16 : 0;
   a.valu_takes_m = mfma ? 0 : 1;
 
   // output-column chunks: more chunks per tile when there are few tiles
   const int est_v = std::max(1, std::min(d.S, shape->n_adapters)) * n_problems;
   const int est_m = std::max(1, (d.T + kMfmaRows - 1) / kMfmaRows) * n_problems;
-  L.decode = mode == MODE_FUSED && vec && tn.decode;
-  a.valu_skip_v = L.decode ? 1 : 0;
-  L.valu = !L.decode || a.valu_takes_m;
   int cv = 1, cm = 1;
   if (mode != MODE_SHRINK) {
-    const int want = L.decode ? tn.decode_items : tn.valu_items;
-    cv = std::min(pow2_floor(std::max(1, want / est_v)), tn.valu_max_chunks);
+    cv = std::min(pow2_floor(std::max(1, tn.valu_items / est_v)), tn.valu_max_chunks);
     cv = std::max(1, std::min(cv, std::max(1, d_out / 256)));
     cm = pow2_floor(std::max(1, tn.mfma_items / est_m));
     cm = std::max(1, std::min(cm, std::max(1, d_out / 512)));
@@ -152,29 +142,21 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   if (mode == MODE_SHRINK) { a.cv = a.cm = 1; a.wv = a.wm = round_up(d_out, 128); }
 
   const int64_t items_m = (int64_t)n_problems * P.L.bound_m * a.cm;
-  const int64_t tiles_v = (int64_t)n_problems * P.L.bound_v * a.cv;
-  const int64_t items_v = (L.decode ? 0 : tiles_v) + (a.valu_takes_m ? items_m : 0);
-  const int64_t groups_d = (tiles_v + kDecodeWaves - 1) / kDecodeWaves;
+  const int64_t items_v = (int64_t)n_problems * ((int64_t)P.L.bound_v * a.cv + (a.valu_takes_m ? items_m : 0));
   L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
-  L.grid_d = L.decode ? round_up((int)std::max<int64_t>(std::min<int64_t>(groups_d, tn.grid_cap), 1), 8) : 0;
-  L.smem_d = L.decode ? decode_smem_bytes(a.kr_max) : 0;
   L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
   L.smem_v = valu_smem_bytes(a.kr_max);
   L.smem_m = mfma ? mfma_smem_bytes(L.jt, d.K) : 0;
   return L;
 }
 
-// MFMA tiles (the long groups) first, then the VALU tiles (decode kernel and/or VALU kernel).
+// MFMA tiles (the long groups) first, then the VALU tiles.
 hipError_t launch_all(int mode, int dtype, const Launch &L, const ApplyArgs &a, hipStream_t stream) {
   if (L.jt > 0) {
     hipError_t e = launch_mfma(mode, L.jt, a, L.grid_m, L.smem_m, stream);
     if (e != hipSuccess) return e;
   }
-  if (L.decode) {
-    hipError_t e = launch_decode(dtype, a, L.grid_d, L.smem_d, stream);
-    if (e != hipSuccess) return e;
-  }
-  return L.valu ? launch_valu(mode, dtype, L.vec, a, L.grid_v, L.smem_v, stream) : hipSuccess;
+  return launch_valu(mode, dtype, L.vec, a, L.grid_v, L.smem_v, stream);
 }
 
 void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Plan &P, const lora_pool *shape) {
@@ -189,7 +171,7 @@ void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Pl
   a.cumlen = P.V.cumlen;
   a.tiles_m = P.V.tiles_m;
   a.tiles_v = P.V.tiles_v;
-  a.rowrec = P.V.rowrec;
+  a.vrec = P.V.vrec;
   a.n = shape->n_adapters;
   a.r = shape->rank;
   a.d_in = shape->d_in;

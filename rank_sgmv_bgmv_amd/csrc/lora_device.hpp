@@ -177,36 +177,49 @@ struct Meta {
 };
 constexpr size_t kMetaBytes = (sizeof(Meta) + 255) & ~size_t(255);
 
+// Original slot index of compacted slot kk of a row, from the record's two pos words.
+__device__ __forceinline__ int rec_pos(uint2 w, int kk) {
+  const uint32_t word = kk < 4 ? w.x : w.y;
+  return int((word >> (8 * (kk & 3))) & 0xffu);
+}
+
 // Fill the tile's rows (token index, compacted slots, scales) into LDS.  VALU
-// tiles carry one (token row, request) record per row; MFMA tiles find their
-// rows' requests by a binary search over the sorted rows' prefix sums, staged
-// in LDS with one parallel load.  Ends with a barrier.
-__device__ inline void setup_rows(const ApplyArgs &a, int4 td, const int2 *rec, int n_active, Meta &M) {
+// tiles read their record (one round of independent loads, then the scales);
+// MFMA tiles find their rows' requests by a binary search over the sorted
+// rows' prefix sums, staged in LDS with one parallel load.  Ends with a barrier.
+__device__ inline void setup_rows(const ApplyArgs &a, int4 td, const int *rec, int n_active, Meta &M) {
   const int tid = threadIdx.x;
   const int p0 = td.x, q0 = td.y, nrows = td.z;
-  if (!rec) {
-    // a tile's rows lie in requests q0 .. q0 + nrows - 1 (each holds >= 1 row)
-    const int nq = min(nrows, n_active - q0);
-    if (tid <= nq) M.cum[tid] = gload<int>(a.cumlen + q0 + tid);
-    __syncthreads();
-  }
-  if (tid < nrows) {
-    int s, t;
-    if (rec) {
-      const int2 rr = gload<int2>(rec + tid);
-      t = rr.x;
-      s = rr.y;
-    } else {
-      const int p = p0 + tid;
-      int lo = 0, hi = min(tid, n_active - 1 - q0);
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (M.cum[mid] <= p) lo = mid; else hi = mid - 1;
+  if (rec) {
+    if (tid < nrows) {
+      const int t = gload<int>(rec + R_T + tid), s = gload<int>(rec + R_S + tid);
+      const int nact = gload<int>(rec + R_NACT);
+      const uint2 pw = gload<uint2>(rec + R_POS + 2 * tid);
+      M.t[tid] = t;
+      for (int kk = 0; kk < nact; ++kk) {
+        const int k = rec_pos(pw, kk);
+        M.pos[tid][kk] = k;
+        M.sc[tid][kk] = a.scale ? gload<float>(a.scale + (int64_t)s * a.K + k) : 1.0f;
+        if (tid == 0) M.a[kk] = gload<int>(rec + R_A + kk);
       }
-      s = gload<int>(a.sseg + q0 + lo);
-      t = gload<int>(a.sst + q0 + lo) + (p - M.cum[lo]);
+      if (tid == 0) M.nact = nact;
     }
-    M.t[tid] = t;
+    __syncthreads();
+    return;
+  }
+  // a tile's rows lie in requests q0 .. q0 + nrows - 1 (each holds >= 1 row)
+  const int nq = min(nrows, n_active - q0);
+  if (tid <= nq) M.cum[tid] = gload<int>(a.cumlen + q0 + tid);
+  __syncthreads();
+  if (tid < nrows) {
+    const int p = p0 + tid;
+    int lo = 0, hi = min(tid, n_active - 1 - q0);
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (M.cum[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    const int s = gload<int>(a.sseg + q0 + lo);
+    M.t[tid] = gload<int>(a.sst + q0 + lo) + (p - M.cum[lo]);
     int kk = 0;
     for (int k = 0; k < a.K; ++k) {
       const int ad = gload<int>(a.idx + (int64_t)s * a.K + k);
@@ -224,7 +237,7 @@ __device__ inline void setup_rows(const ApplyArgs &a, int4 td, const int2 *rec, 
 // Zero the intermediate columns of the empty slots of every row of a tile
 // (lora_shrink writes every column of a touched row).
 __device__ inline void zero_empty_slots(const ApplyArgs &a, int nrows, const Meta &M) {
-  for (int e = threadIdx.x; e < nrows * a.K; e += kThreads) {
+  for (int e = threadIdx.x; e < nrows * a.K; e += blockDim.x) {
     const int m = e / a.K, k = e % a.K;
     bool used = false;
     for (int kk = 0; kk < M.nact; ++kk) used |= (M.pos[m][kk] == k);
@@ -283,44 +296,62 @@ __device__ __forceinline__ float wave_sum_scatter(float (&v)[NV]) {
   return s;
 }
 
-// y[0 .. RT) += acc, rounded once to T, with one vector access when aligned;
-// y is at byte offset `off` from p.
-template <typename T, bool VEC, int RT>
-__device__ __forceinline__ void add_store_rt(T *p, const float (&acc)[RT], uint32_t off = 0) {
-  if constexpr (VEC && sizeof(T) == 2 && RT == 8) {
-    uint4 y = gload_at<uint4>(p, off);
-    y.x = pack_bf2(bf_lo(y.x) + acc[0], bf_hi(y.x) + acc[1]);
-    y.y = pack_bf2(bf_lo(y.y) + acc[2], bf_hi(y.y) + acc[3]);
-    y.z = pack_bf2(bf_lo(y.z) + acc[4], bf_hi(y.z) + acc[5]);
-    y.w = pack_bf2(bf_lo(y.w) + acc[6], bf_hi(y.w) + acc[7]);
-    gstore_at(p, off, y);
-  } else if constexpr (VEC && sizeof(T) == 2 && RT == 4) {
-    uint2 y = gload_at<uint2>(p, off);
-    y.x = pack_bf2(bf_lo(y.x) + acc[0], bf_hi(y.x) + acc[1]);
-    y.y = pack_bf2(bf_lo(y.y) + acc[2], bf_hi(y.y) + acc[3]);
-    gstore_at(p, off, y);
-  } else if constexpr (VEC && sizeof(T) == 2 && RT == 2) {
-    const uint32_t y = gload_at<uint32_t>(p, off);
-    gstore_at(p, off, pack_bf2(bf_lo(y) + acc[0], bf_hi(y) + acc[1]));
-  } else if constexpr (VEC && sizeof(T) == 4 && RT >= 4) {
+// RT consecutive outputs of one y row, held between a load and the
+// read-modify-write that adds the result (rounded once to T): one vector
+// access when the vector path allows it, else element by element.  p is a
+// (wave-uniform) row base, off the byte offset of the first output.
+template <typename T, bool VEC, int RT> struct YRun {
+  static constexpr bool kVec = VEC && RT * sizeof(T) >= 4 && RT * sizeof(T) <= 16;
+  typedef typename Raw<kVec ? RT * sizeof(T) : 4>::type R;
+  R v[kVec ? 1 : RT];
+  __device__ __forceinline__ void load(const T *p, uint32_t off) {
+    if constexpr (kVec) {
+      v[0] = gload_at<R>(p, off);
+    } else {
 #pragma unroll
-    for (int i = 0; i < RT; i += 4) {
-      float4 y = gload_at<float4>(p, off + 4 * i);
-      y.x += acc[i]; y.y += acc[i + 1]; y.z += acc[i + 2]; y.w += acc[i + 3];
-      gstore_at(p, off + 4 * i, y);
-    }
-  } else if constexpr (VEC && sizeof(T) == 4 && RT == 2) {
-    float2 y = gload_at<float2>(p, off);
-    y.x += acc[0]; y.y += acc[1];
-    gstore_at(p, off, y);
-  } else {
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const uint32_t o = off + i * sizeof(T);
-      if constexpr (sizeof(T) == 2) gstore_at(p, o, f_to_bf(bf_to_f(gload_at<uint16_t>(p, o)) + acc[i]));
-      else gstore_at(p, o, gload_at<float>(p, o) + acc[i]);
+      for (int i = 0; i < RT; ++i) {
+        if constexpr (sizeof(T) == 2) v[i] = gload_at<uint16_t>(p, off + 2 * i);
+        else v[i] = gload_at<uint32_t>(p, off + 4 * i);
+      }
     }
   }
+  __device__ __forceinline__ void add_store(T *p, uint32_t off, const float (&acc)[RT]) const {
+    if constexpr (kVec) {
+      constexpr int W = RT * sizeof(T) / 4;  // 32-bit words
+      uint32_t w[W];
+      if constexpr (W == 1) w[0] = v[0];
+      else {
+#pragma unroll
+        for (int i = 0; i < W; ++i) w[i] = v[0][i];
+      }
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        if constexpr (sizeof(T) == 2) w[i] = pack_bf2(bf_lo(w[i]) + acc[2 * i], bf_hi(w[i]) + acc[2 * i + 1]);
+        else w[i] = __float_as_uint(__uint_as_float(w[i]) + acc[i]);
+      }
+      R o;
+      if constexpr (W == 1) o = w[0];
+      else {
+#pragma unroll
+        for (int i = 0; i < W; ++i) o[i] = w[i];
+      }
+      gstore_at(p, off, o);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        if constexpr (sizeof(T) == 2) gstore_at(p, off + 2 * i, f_to_bf(bf_to_f(uint16_t(v[i])) + acc[i]));
+        else gstore_at(p, off + 4 * i, __uint_as_float(v[i]) + acc[i]);
+      }
+    }
+  }
+};
+
+// y[0 .. RT) += acc at byte offset off from p.
+template <typename T, bool VEC, int RT>
+__device__ __forceinline__ void add_store_rt(T *p, const float (&acc)[RT], uint32_t off = 0) {
+  YRun<T, VEC, RT> y;
+  y.load(p, off);
+  y.add_store(p, off, acc);
 }
 
 }  // namespace lora

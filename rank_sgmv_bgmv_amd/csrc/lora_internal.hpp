@@ -12,13 +12,30 @@ namespace lora {
 
 constexpr int kPlanThreads = 1024;  // one workgroup builds the plan
 constexpr int kThreads = 256;       // apply kernels: 4 wave64s per workgroup
+constexpr int kValuThreads = 256;   // VALU kernel workgroup
 constexpr int kMfmaRows = 64;       // rows per MFMA tile (16 per wave)
-constexpr int kValuRows = 16;       // rows per VALU tile
+constexpr int kValuRows = 4;        // rows per VALU tile (one row block: heavy adapters become several tiles)
 constexpr int kMfmaMinRows = 17;    // adapter groups with at least this many rows get MFMA tiles
 constexpr int kRowBlock = 4;        // rows per VALU pass (register budget of the VALU tile body)
 constexpr int kMfmaMaxRank = 128;   // MFMA tiles serve ranks 16, 32, 64, 128
+constexpr int kMfmaMinBatch = 128;  // batches of fewer rows leave every tile to the VALU kernel (one launch)
 constexpr int kMfmaMaxSlotRank = 512;
 constexpr int kMaxLdsBytes = 160 * 1024;  // LDS a gfx950 workgroup may allocate
+
+// Record of one VALU tile, written by the plan (int32 words): everything the
+// apply kernels need to start on the tile except the scales, in one 128-byte
+// read.  pos holds, per row and compacted slot, the original slot index (one
+// byte each).
+enum {
+  R_NROWS = 0,   // rows of the tile (1 .. kValuRows)
+  R_NACT = 1,    // valid slots (adapters) of the tile's rows
+  R_T = 2,       // token row of each row          [kValuRows]
+  R_S = 6,       // request of each row            [kValuRows]
+  R_A = 10,      // adapter of each compacted slot [LORA_MAX_SLOTS]
+  R_POS = 18,    // bytes pos[row][slot]           [kValuRows * LORA_MAX_SLOTS / 4 words]
+  kRecWords = 32
+};
+static_assert(kValuRows == 4 && LORA_MAX_SLOTS == 8, "tile record layout assumes 4 rows and 8 slots");
 
 // Plan header words (int32).
 enum {
@@ -36,7 +53,7 @@ constexpr int kPlanMagic = 0x4c6f5241;  // "LoRA"
 
 // Byte offsets of the plan arrays inside the workspace.
 struct PlanLayout {
-  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, tiles_m, tiles_v, rowrec, total;
+  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, tiles_m, tiles_v, vrec, total;
   int S, T, n, bound_m, bound_v;
   size_t lds_bytes;  // LDS the plan kernel uses for its working arrays (0: they stay in global memory)
 };
@@ -67,7 +84,7 @@ inline PlanLayout plan_layout(int S, int T, int n) {
   L.toff_v = take(sizeof(int) * (size_t(S) + 2));
   L.tiles_m = take(sizeof(int4) * size_t(L.bound_m));
   L.tiles_v = take(sizeof(int4) * size_t(L.bound_v));
-  L.rowrec = take(sizeof(int2) * kValuRows * size_t(L.bound_v));
+  L.vrec = take(sizeof(int) * kRecWords * size_t(L.bound_v));
   L.total = off;
   // working arrays: start, key, sseg, sst (S+1 each), cumlen, gtmp, gstart, toff_m, toff_v (S+2 each),
   // cnt, cur (n+2 each)
@@ -80,7 +97,7 @@ inline PlanLayout plan_layout(int S, int T, int n) {
 struct PlanView {
   int *hdr, *start, *key, *cnt, *cur, *sseg, *sst, *cumlen, *gtmp, *gstart, *toff_m, *toff_v;
   int4 *tiles_m, *tiles_v;
-  int2 *rowrec;  // per VALU tile: (token row, request) of each of its rows
+  int *vrec;  // per VALU tile: a record of kRecWords words
   int S, T, n, K, per_token;
   int lds_mode;
 };
@@ -102,7 +119,7 @@ inline PlanView plan_view(void *ws, const PlanLayout &L, int K, int per_token) {
   P.toff_v = reinterpret_cast<int *>(b + L.toff_v);
   P.tiles_m = reinterpret_cast<int4 *>(b + L.tiles_m);
   P.tiles_v = reinterpret_cast<int4 *>(b + L.tiles_v);
-  P.rowrec = reinterpret_cast<int2 *>(b + L.rowrec);
+  P.vrec = reinterpret_cast<int *>(b + L.vrec);
   P.S = L.S; P.T = L.T; P.n = L.n; P.K = K; P.per_token = per_token;
   P.lds_mode = L.lds_bytes > 0;
   return P;
@@ -119,7 +136,7 @@ struct ApplyArgs {
   // plan (read only)
   const int *hdr, *sseg, *sst, *cumlen;
   const int4 *tiles_m, *tiles_v;
-  const int2 *rowrec;
+  const int *vrec;
   // shape shared by every problem
   int n, r, d_in, d_out;
   // problems
@@ -134,11 +151,9 @@ struct ApplyArgs {
   // layout of dynamic LDS
   int kr_max;      // max_slots * rank (row stride of the VALU intermediate)
   int valu_takes_m;  // the VALU kernel also runs the MFMA-sized tiles (no MFMA kernel launched)
-  int valu_skip_v;   // the VALU kernel leaves the VALU tiles to the decode kernel
 };
 
 size_t valu_smem_bytes(int kr_max);
-size_t decode_smem_bytes(int kr_max);
 size_t mfma_smem_bytes(int jt, int slots);
 
 hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, const int *idx, hipStream_t stream);
@@ -146,9 +161,6 @@ hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, 
 // VALU kernel: dtype LORA_F32 / LORA_BF16, vec = 16-byte vector path.
 hipError_t launch_valu(int mode, int dtype, bool vec, const ApplyArgs &args, int grid, size_t smem,
                        hipStream_t stream);
-// Decode kernel (fused mode, vector path): one wave per VALU-tile work item.
-constexpr int kDecodeWaves = kThreads / 64;
-hipError_t launch_decode(int dtype, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
 // MFMA kernel (bf16, vector path): jt = rank / 16 in {1, 2, 4, 8}.
 hipError_t launch_mfma(int mode, int jt, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
 

@@ -20,8 +20,9 @@
 //   5. group boundaries; a group of >= kMfmaMinRows rows is cut into MFMA
 //      tiles of kMfmaRows rows, a smaller one into VALU tiles of kValuRows;
 //   6. one tile descriptor per tile: {first row, first request, rows, group end},
-//      and for VALU tiles one (token row, request) record per row, so the
-//      apply kernel starts streaming after two dependent loads.
+//      and for VALU tiles a record with each row's token row and request and
+//      the tile's compacted adapters, so the apply kernels start streaming
+//      after one read (two with per-slot scales).
 // Rows never move: a tile names rows by (sorted request, offset) and the apply
 // kernels read and write x / y rows in place.
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
   if (tid == 0) { toff_m[n_groups] = nt_m; toff_v[n_groups] = nt_v; }
   __syncthreads();
 
-  // 6. tile descriptors; VALU tiles also get one (token row, request) record per row
+  // 6. tile descriptors; VALU tiles also get a record
   for (int u = tid; u < nt_m + nt_v; u += kPlanThreads) {
     const bool is_m = u < nt_m;
     const int uu = is_m ? u : u - nt_m;
@@ -246,12 +247,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
       P.tiles_m[uu] = d;
     } else {
       P.tiles_v[uu] = d;
-      int q = q0;
+      // the tile's record: rows, requests, compacted slots (all rows of a tile
+      // share their adapters: one adapter, or one stacking request)
+      int *R = P.vrec + (int64_t)uu * kRecWords;
+      int q = q0, nact = 0;
+      for (int w = 0; w < kValuRows * LORA_MAX_SLOTS / 4; ++w) R[R_POS + w] = 0;
+      uint8_t *pos = reinterpret_cast<uint8_t *>(R + R_POS);
       for (int i = 0; i < nrows; ++i) {
         const int p = p0 + i;
         while (cumlen[q + 1] <= p) ++q;
-        P.rowrec[(int64_t)uu * kValuRows + i] = make_int2(sst[q] + (p - cumlen[q]), sseg[q]);
+        const int s = sseg[q];
+        R[R_T + i] = sst[q] + (p - cumlen[q]);
+        R[R_S + i] = s;
+        int kk = 0;
+        for (int k = 0; k < P.K; ++k) {
+          const int ad = idx[(int64_t)s * P.K + k];
+          if (ad < 0 || ad >= P.n) continue;
+          if (i == 0) R[R_A + kk] = ad;
+          pos[i * LORA_MAX_SLOTS + kk] = uint8_t(k);
+          ++kk;
+        }
+        if (i == 0) nact = kk;
       }
+      R[R_NROWS] = nrows;
+      R[R_NACT] = nact;
     }
   }
 

@@ -1,20 +1,26 @@
-// VALU apply kernel: decode (BGMV) tiles of up to 16 rows, plus every tile when
-// the MFMA path does not apply (fp32, ranks other than 16/32/64/128, unaligned
-// or odd sizes).  Computes y += scale * (x A_i^T) B_i^T for the tile's rows.
+// VALU apply kernel: decode (BGMV) tiles of up to 4 rows of one adapter group,
+// plus every tile when the MFMA path does not apply (fp32, ranks other than
+// 16/32/64/128, unaligned or odd sizes).  Computes y += scale * (x A_i^T) B_i^T
+// for the tile's rows.
 //
 // "Serving several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
 // alongside": the unmerged form adds x A^T B^T to x W^T; "Exercises" (four
 // requests): the requests that share a LoRA form one group and get their own
 // x A^T B^T, written back to their original rows.
 //
+// One workgroup per (problem, tile, output chunk).  A decode tile is a gather
+// of one adapter's A and B with very little arithmetic per byte, so both
+// phases are written to keep many independent 16-byte loads in flight:
 // Shrink: each wave owns four rank rows of A per pass and its lanes split d_in
-// into 16-byte pieces, several pieces of A and x in flight per lane; the wave's
-// partial sums are combined by a butterfly reduce-scatter over lanes (no LDS,
-// no barrier) and land in LDS as the fp32 rank-r intermediate.  Expand: each
-// thread owns a few consecutive outputs and the whole rank, streams those
-// contiguous B rows with 16-byte loads, reads the intermediate from LDS as a
-// broadcast, and updates y in place with one vector access per row: no
-// cross-lane reduction, no staging.
+// into 16-byte pieces; the wave's partial sums are combined by a butterfly
+// reduce-scatter over lanes (no LDS, no barrier) and land in LDS as the
+// rank-r intermediate.  Expand: each thread owns short runs of consecutive
+// outputs and the whole rank, streams those contiguous B rows, reads the
+// intermediate from LDS as a broadcast, and updates y in place (loaded at
+// the start of the round) with one vector access per run: no cross-lane
+// reduction, no staging.
+
+#include <type_traits>
 
 #include "lora_device.hpp"
 
@@ -24,32 +30,39 @@ namespace {
 // ------------------------------------------------------------ VALU tile --
 constexpr int kJPW = 4;  // rank rows a wave owns per pass of the VALU shrink
 
+// Type of the intermediate kept in LDS: the fused bf16 vector path keeps it in
+// bf16 (as the MFMA path does) so the expand multiplies packed pairs; every
+// other path keeps fp32.
+template <typename T, bool VEC, int MODE>
+using InterT = typename std::conditional<MODE == MODE_FUSED && VEC && sizeof(T) == 2, uint16_t, float>::type;
+
 // Shrink for MB rows (nb of them real): wave w owns rank rows j0 .. j0+3 of a
 // pass, its lanes split d_in into 16-byte pieces (lane l takes pieces l,
 // l+64, ...), UB pieces per lane per round for x and A each, so a round keeps
-// UB*(MB+4) independent 16-byte loads in flight per lane.  The MB*4 partial
-// sums per lane are reduced over the wave by wave_sum_scatter; no LDS traffic
-// and no barrier inside.
+// UB*(MB+4) independent 16-byte loads in flight per lane.  Loads use clamped
+// (always valid) addresses; pieces past the end are masked to zero.  The MB*4
+// partial sums per lane are reduced over the wave by wave_sum_scatter; no LDS
+// traffic and no barrier inside.
 template <typename T, bool VEC, int MB, int MODE>
 __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
-                            float *s_v) {
+                            InterT<T, VEC, MODE> *s_v) {
   typedef VOps<T, VEC> O;
   typedef typename O::V V;
   constexpr int E = O::E;
   constexpr int NV = MB * kJPW;
   constexpr int UB = MB <= 2 ? 4 : 2;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int r = a.r, d_in = a.d_in, KR = a.kr_max, nact = uniform(M.nact);
   const int nvx = d_in / E;
-  const T *__restrict__ Ab = static_cast<const T *>(pr.A);
+  const uint32_t row_bytes = uint32_t(d_in) * sizeof(T);
   const T *xrow[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
     xrow[m] = static_cast<const T *>(pr.x) + (int64_t)uniform(M.t[m0 + (m < nb ? m : 0)]) * pr.ldx;
 
   for (int kk = 0; kk < nact; ++kk) {
-    const T *__restrict__ Aa = Ab + (int64_t)uniform(M.a[kk]) * r * d_in;
-    for (int j0 = w * kJPW; j0 < r; j0 += 4 * kJPW) {
+    const T *Aa = static_cast<const T *>(pr.A) + (int64_t)uniform(M.a[kk]) * r * d_in;
+    for (int j0 = w * kJPW; j0 < r; j0 += (kValuThreads / 64) * kJPW) {
       float acc[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = 0.f;
@@ -58,12 +71,15 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
           const int cv = c0 + 64 * u;
-          const bool ok = cv < nvx;
+          const uint32_t off = uint32_t(min(cv, nvx - 1)) * (E * sizeof(T));
 #pragma unroll
-          for (int m = 0; m < MB; ++m) xv[u][m] = (ok && m < nb) ? O::load(xrow[m] + (int64_t)cv * E) : O::zero();
+          for (int m = 0; m < MB; ++m) xv[u][m] = gload_at<V>(xrow[m], off);
 #pragma unroll
-          for (int i = 0; i < kJPW; ++i)
-            av[u][i] = (ok && j0 + i < r) ? O::load(Aa + (int64_t)(j0 + i) * d_in + (int64_t)cv * E) : O::zero();
+          for (int i = 0; i < kJPW; ++i) av[u][i] = gload_at<V>(Aa, uint32_t(min(j0 + i, r - 1)) * row_bytes + off);
+          if (cv >= nvx) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m) xv[u][m] = O::zero();
+          }
         }
 #pragma unroll
         for (int u = 0; u < UB; ++u)
@@ -77,8 +93,10 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
         const int m = lane / kJPW, j = j0 + lane % kJPW;
         if (m < nb && j < r) {
           const float vs = val * M.sc[m0 + m][kk];
-          if (MODE == MODE_SHRINK)
+          if constexpr (MODE == MODE_SHRINK)
             gstore(a.v + (int64_t)M.t[m0 + m] * a.ldv + (int64_t)M.pos[m0 + m][kk] * r + j, vs);
+          else if constexpr (sizeof(InterT<T, VEC, MODE>) == 2)
+            s_v[m * KR + kk * r + j] = f_to_bf(vs);
           else
             s_v[m * KR + kk * r + j] = vs;
         }
@@ -87,53 +105,97 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
   }
 }
 
-// Expand for MB rows: thread owns RT consecutive outputs o .. o+RT-1 and all
-// of the rank, so each output is finished inside one lane (no cross-lane
-// reduction, no staging): per slot it loads the RT contiguous B rows
-// (RT * rank elements) in rounds of 16 vectors, multiplies them with the
-// intermediate read from LDS (a broadcast: every lane reads the same address)
-// and finally adds the result to y with one vector access per row.
-template <typename T, bool VEC, int MB, int RT>
+// B vectors a lane keeps in flight per expand round: 16, halved for four rows
+// and for an fp32 intermediate (which unpacks B to fp32 in registers).
+template <int MB, int IT_BYTES>
+constexpr int expand_nvb() { return (IT_BYTES == 2 ? 16 : 8) / (MB >= 4 ? 2 : 1); }
+
+// Expand for MB rows.  A round gives each thread NBLK blocks of RT
+// consecutive outputs (block b starts at o0 + b * 256 * RT), so one load
+// instruction of the workgroup covers 256 * RT contiguous B rows and each lane
+// reads a short contiguous run of RT rows (about 64 bytes: wider per-lane runs
+// make every load instruction touch many more cache lines).  Each output is
+// finished inside one lane: per slot the thread loads its B rows (up to NVB
+// 16-byte vectors at once), multiplies them with the intermediate read from
+// LDS (a broadcast: every lane reads the same address) and finally adds the
+// result to the y values it loaded at the start of the round.
+template <typename T, bool VEC, int MB, int RT, int NBLK, int MODE>
 __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
-                            const float *s_v, int o_lo, int o_hi) {
+                            const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi) {
   typedef VOps<T, VEC> O;
   typedef typename O::V V;
+  typedef InterT<T, VEC, MODE> IT;
   constexpr int E = O::E;
-  constexpr int NVB = MB >= 4 ? 8 : 16;  // B vectors in flight per lane per round
-  constexpr int JB = NVB / RT >= 1 ? NVB / RT : 1;  // vectors per output row per round
+  constexpr int NVB = expand_nvb<MB, sizeof(IT)>();  // B vectors in flight per lane per round
+  constexpr int JB = NVB / (RT * NBLK) >= 1 ? NVB / (RT * NBLK) : 1;  // vectors per output row per round
+  constexpr int BS = kValuThreads * RT;  // block stride (outputs)
   const int tid = threadIdx.x;
   const int r = a.r, d_out = a.d_out, KR = a.kr_max, nact = uniform(M.nact);
   const int nvr = r / E;
-  const T *__restrict__ Bb = static_cast<const T *>(pr.B);
+  const uint32_t brow_bytes = uint32_t(r) * sizeof(T);
   T *yrow[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
     yrow[m] = static_cast<T *>(pr.y) + (int64_t)uniform(M.t[m0 + (m < nb ? m : 0)]) * pr.ldy;
-  for (int o = o_lo + tid * RT; o < o_hi; o += kThreads * RT) {
-    float acc[MB][RT];
+  for (int o0 = o_lo + tid * RT; o0 < o_hi; o0 += BS * NBLK) {
+    // blocks past o_hi load a valid row (the chunk's last RT rows) and store nothing
+    int ob[NBLK];
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) ob[b] = min(o0 + b * BS, o_hi - RT);
+    YRun<T, VEC, RT> yv[MB][NBLK];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int i = 0; i < RT; ++i) acc[m][i] = 0.f;
+      for (int b = 0; b < NBLK; ++b)
+        if (m < nb) yv[m][b].load(yrow[m], uint32_t(ob[b]) * sizeof(T));
+    float acc[MB][NBLK][RT];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int i = 0; i < RT; ++i) acc[m][b][i] = 0.f;
     for (int kk = 0; kk < nact; ++kk) {
-      const T *__restrict__ Bk = Bb + (int64_t)uniform(M.a[kk]) * d_out * r;
-      const float *vk = s_v + kk * r;
+      const T *Bk = static_cast<const T *>(pr.B) + (int64_t)uniform(M.a[kk]) * d_out * r;
+      const IT *vk = s_v + kk * r;
       for (int jv0 = 0; jv0 < nvr; jv0 += JB) {
-        V bv[RT][JB];
+        V bv[NBLK][RT][JB];
 #pragma unroll
-        for (int i = 0; i < RT; ++i)
+        for (int b = 0; b < NBLK; ++b)
 #pragma unroll
-          for (int jj = 0; jj < JB; ++jj)
-            bv[i][jj] = (jv0 + jj < nvr) ? O::load(Bk + (o + i) * r + (jv0 + jj) * E) : O::zero();
+          for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj)
+              bv[b][i][jj] = gload_at<V>(Bk, uint32_t(ob[b] + i) * brow_bytes +
+                                                 uint32_t(min(jv0 + jj, nvr - 1)) * (E * sizeof(T)));
+        // vectors past the rank contribute zero (the loads above stay unconditional,
+        // so they are all in flight before the first multiply)
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          if (jv0 + jj >= nvr) {
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+              for (int i = 0; i < RT; ++i) bv[b][i][jj] = O::zero();
+          }
+        }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
           if (m < nb) {
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
-              if (jv0 + jj < nvr) {
-                const float *vp = vk + m * KR + (jv0 + jj) * E;
+              const IT *vp = vk + m * KR + min(jv0 + jj, nvr - 1) * E;
+              if constexpr (sizeof(IT) == 2) {
+                const V vv = *reinterpret_cast<const V *>(vp);
 #pragma unroll
-                for (int i = 0; i < RT; ++i) acc[m][i] = O::dotf(vp, bv[i][jj], acc[m][i]);
+                for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+                  for (int i = 0; i < RT; ++i) acc[m][b][i] = O::dot(vv, bv[b][i][jj], acc[m][b][i]);
+              } else {
+#pragma unroll
+                for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+                  for (int i = 0; i < RT; ++i) acc[m][b][i] = O::dotf(vp, bv[b][i][jj], acc[m][b][i]);
               }
             }
           }
@@ -142,32 +204,48 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m)
-      if (m < nb) add_store_rt<T, VEC, RT>(yrow[m] + o, acc[m]);
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+        if (m < nb && o0 + b * BS < o_hi) yv[m][b].add_store(yrow[m], uint32_t(ob[b]) * sizeof(T), acc[m][b]);
   }
 }
 
-template <typename T, bool VEC, int MB>
+// Outputs per block: rows of about 64 bytes per lane, never more than the
+// vector width, which divides d_out on the vector path (so a block never
+// straddles the end of a row).  Blocks per round: about 16 B vectors per lane
+// (8 with four rows).  The scalar path takes one output per thread.
+template <typename T, bool VEC, int MB, int MODE>
 __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
-                               const float *s_v, int o_lo, int o_hi) {
-  // outputs per thread: enough that a thread's B rows fill 8 vectors, at most
-  // 16 accumulators (MB rows x RT outputs) per lane, and never more than the
-  // vector width, which divides d_out on the vector path (so an RT-group never
-  // straddles the end of a row).  The scalar path takes one output per thread.
+                               const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi) {
   constexpr int E = VOps<T, VEC>::E;
   if constexpr (!VEC) {
-    valu_expand<T, VEC, MB, 1>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
     return;
+  } else {
+    const int row_bytes = a.r * int(sizeof(T));
+    const int rt = min(max(64 / row_bytes, 1), E);
+    const int vpr = a.r / E;
+    int nblk = expand_nvb<MB, sizeof(InterT<T, VEC, MODE>)>() / (rt * vpr);
+    nblk = nblk >= 4 ? 4 : nblk >= 2 ? 2 : 1;
+    while (nblk > 1 && MB * rt * nblk > 16) nblk >>= 1;  // at most 16 accumulators per lane
+    // only the (RT, NBLK) pairs within the accumulator budget are compiled
+#define LORA_EXPAND(RT_, NB_)                                                         \
+  if constexpr (MB * RT_ * NB_ <= 16) {                                               \
+    if (rt == RT_ && nblk == NB_) {                                                   \
+      valu_expand<T, VEC, MB, RT_, NB_, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);     \
+      return;                                                                         \
+    }                                                                                 \
   }
-  const int q = min(min((16 * E) / a.r, 32 / MB), E);
-  if (q >= 8) valu_expand<T, VEC, MB, 8>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-  else if (q >= 4) valu_expand<T, VEC, MB, 4>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-  else if (q >= 2) valu_expand<T, VEC, MB, 2>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-  else valu_expand<T, VEC, MB, 1>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    LORA_EXPAND(4, 4) LORA_EXPAND(4, 2) LORA_EXPAND(4, 1) LORA_EXPAND(2, 4) LORA_EXPAND(2, 2)
+    LORA_EXPAND(2, 1) LORA_EXPAND(1, 4) LORA_EXPAND(1, 2)
+#undef LORA_EXPAND
+    valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+  }
 }
 
 template <typename T, bool VEC, int MODE>
 __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, Meta &M,
-                          float *s_v) {
+                          InterT<T, VEC, MODE> *s_v) {
   const int tid = threadIdx.x;
   const int r = a.r, KR = a.kr_max, nact = M.nact;
   if (MODE == MODE_SHRINK) zero_empty_slots(a, nrows, M);
@@ -179,16 +257,16 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
       else valu_shrink<T, VEC, 4, MODE>(a, pr, m0, nb, M, s_v);
     } else {
       // expand only: the caller's intermediate (compacted slots) into LDS
-      for (int w = tid; w < nb * nact * r; w += kThreads) {
+      for (int w = tid; w < nb * nact * r; w += kValuThreads) {
         const int m = w / (nact * r), rem = w % (nact * r), kk = rem / r, j = rem % r;
         s_v[m * KR + kk * r + j] = gload<float>(a.v + (int64_t)M.t[m0 + m] * a.ldv + (int64_t)M.pos[m0 + m][kk] * r + j);
       }
     }
     if (MODE == MODE_SHRINK) continue;
     __syncthreads();  // the intermediate of this row block is complete
-    if (nb <= 1) valu_expand_rt<T, VEC, 1>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-    else if (nb <= 2) valu_expand_rt<T, VEC, 2>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-    else valu_expand_rt<T, VEC, 4>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    if (nb <= 1) valu_expand_rt<T, VEC, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    else if (nb <= 2) valu_expand_rt<T, VEC, 2, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    else valu_expand_rt<T, VEC, 4, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
     __syncthreads();  // before the next row block overwrites the intermediate
   }
 }
@@ -197,14 +275,14 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
 // At least four waves per SIMD (<= 128 VGPRs): the per-tile phases are short
 // dependent chains, and occupancy is what overlaps them.
 template <typename T, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void valu_kernel(ApplyArgs a) {
+__global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Meta &M = *reinterpret_cast<Meta *>(smem);
-  float *s_v = reinterpret_cast<float *>(smem + kMetaBytes);
+  InterT<T, VEC, MODE> *s_v = reinterpret_cast<InterT<T, VEC, MODE> *>(smem + kMetaBytes);
   const int n_m = gload<int>(a.hdr + H_TILES_M), n_v = gload<int>(a.hdr + H_TILES_V);
   const int n_active = gload<int>(a.hdr + H_ACTIVE);
   // VALU tiles first; MFMA-sized tiles too when the MFMA kernel does not run
-  const int64_t items_v = a.valu_skip_v ? 0 : (int64_t)n_v * a.cv;
+  const int64_t items_v = (int64_t)n_v * a.cv;
   const int64_t items_m = a.valu_takes_m ? (int64_t)n_m * a.cm : 0;
   const int64_t per_prob = items_v + items_m;
   walk_items(per_prob * a.n_problems, [&](int64_t item) {
@@ -217,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(ApplyArgs a) {
     const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
     const int4 td = gload<int4>(is_m ? a.tiles_m + tile : a.tiles_v + tile);
     const int o_lo = chunk * width, o_hi = min(a.d_out, o_lo + width);
-    setup_rows(a, td, is_m ? nullptr : a.rowrec + (int64_t)tile * kValuRows, n_active, M);
+    setup_rows(a, td, is_m ? nullptr : a.vrec + (int64_t)tile * kRecWords, n_active, M);
     if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) valu_tile<T, VEC, MODE>(a, pr, td.z, o_lo, o_hi, M, s_v);
   });
 }
@@ -230,7 +308,7 @@ hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t str
       hipFuncSetAttribute(reinterpret_cast<const void *>(&valu_kernel<T, VEC, M>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
-  hipLaunchKernelGGL((valu_kernel<T, VEC, M>), dim3(grid), dim3(kThreads), smem, stream, a);
+  hipLaunchKernelGGL((valu_kernel<T, VEC, M>), dim3(grid), dim3(kValuThreads), smem, stream, a);
   return hipGetLastError();
 }
 

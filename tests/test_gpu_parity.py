@@ -64,6 +64,9 @@ GRID = {
     "bf16_wide_out_chunks": dict(dtype=W.BF16, n=3, r=16, d_in=256, d_out=4096, S=2, min_len=1, max_len=3),
     "bf16_gaps_empty_slots": dict(dtype=W.BF16, n=8, r=32, d_in=96, d_out=160, S=12, K=2, min_len=0, max_len=25,
                                   gaps=True, p_empty=0.5, with_scale=True),
+    # fewer than 128 rows: the VALU kernel also takes the groups of >= 17 rows
+    "bf16_small_batch_long_groups": dict(dtype=W.BF16, n=2, r=16, d_in=256, d_out=512, S=3, min_len=20,
+                                         max_len=40, with_scale=True),
 }
 
 
