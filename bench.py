@@ -40,6 +40,30 @@ from rank_sgmv_bgmv_amd import accounting  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs
+# of `bench.py --only decode32` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for a plain copy of known size
+# (`bench.py --copy-calibration`: 256 MiB read + 256 MiB written per launch
+# reads FETCH_SIZE 131084 KiB and WRITE_SIZE 262144 KiB, so x2.0 and x1.0).
+# Valid only for the kernel sources they were taken on: reported as null once
+# those sources change.
+TRAFFIC_SOURCES = ["rank_sgmv_bgmv_amd/csrc/lora_valu.hip", "rank_sgmv_bgmv_amd/csrc/lora_device.hpp",
+                   "rank_sgmv_bgmv_amd/csrc/lora_internal.hpp"]
+MEASURED_TRAFFIC = {"sources_sha256_16": "b78310c3b0f1c19a", "fetch_kib": 181122.0, "write_kib": 16384.0,
+                    "fetch_scale": 2.0, "write_scale": 1.0}
+
+
+def measured_traffic_bytes():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    m = MEASURED_TRAFFIC
+    if h.hexdigest()[:16] != m["sources_sha256_16"]:
+        return None
+    return m["fetch_kib"] * 1024 * m["fetch_scale"] + m["write_kib"] * 1024 * m["write_scale"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -274,6 +298,21 @@ def cpu_baseline_decode(state, layers_sample=8, min_seconds=12.0):
                       f"({dt:.1f} s wall, {cores} threads); tokens/s scaled to 32 layers"}
 
 
+def copy_calibration(dev, mib=256, reps=5):
+    """A plain device copy of known size: each launch reads and writes `mib` MiB.
+    Profiled with the FETCH_SIZE / WRITE_SIZE counters it gives the factor that
+    turns those counters into HBM bytes for the LoRA kernels."""
+    torch = torch_mod()
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "launches": reps}
+
+
 # --------------------------------------------------------------------- main --
 def main():
     ap = argparse.ArgumentParser()
@@ -282,6 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only; requests would shard across GPUs "
@@ -289,9 +330,12 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     torch = torch_mod()
+    dev = "cuda:0"
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(dev)))
+        return
     import rank_sgmv_bgmv_amd as L
     L.lib()
-    dev = "cuda:0"
     only = set(s for s in args.only.split(",") if s)
     want = lambda k: not only or k in only  # noqa: E731
 
@@ -344,7 +388,8 @@ def main():
                                                   "launch per step", "global_batch": 64, "seq_len": 1,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": head["apply_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["apply_GBps"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": head["apply_GBps"] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic_bytes() if head is not None and "decode" in head["workload"] else None,
                      "kernel": "valu_kernel<bf16, vec, fused> (shrink + expand of every decode tile, one launch for all 32 layers)",
                      "bytes_per_launch": head["apply_bytes_per_launch"], "avg_launch_us": head["apply_kernel_us"]},
         "cpu_baseline": cpu,

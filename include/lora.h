@@ -6,15 +6,15 @@
  * increment W' = W + BA with A of shape r x d and B of shape d x r, and the
  * unmerged form adds x A^T B^T to the base output x W^T in every adapted
  * layer.  Here A is r x d_in and B is d_out x r.  The same page, self-test
- * answer on mixing LoRAs and the "Exercises" answer on four requests: every
- * request carries its own LoRA index; the low-rank products are grouped by
- * LoRA index, one kernel handles every group, and the results are added back
- * into the base output in the original row order.  "Punica: Multi-Tenant LoRA
- * Serving" (contribution 1) names the same idea segmented gather
- * matrix-vector (SGMV) kernels for heterogeneous LoRA batches.  Stacked LoRAs
- * are extra alongside computations that are summed (comparison table,
- * "Stacking several LoRAs"); a per-slot scale is the swappable scalar of the
- * timestep-varying LoRA weight (same section, the paragraph on diffusion).
+ * answer on mixing LoRAs and the "Exercises" answer on four requests: each
+ * request names its own adapter; rows are partitioned by adapter, a single
+ * kernel covers all partitions, and each result goes back to the row it came
+ * from.  "Punica: Multi-Tenant LoRA Serving" (contribution 1) describes the
+ * same scheme as segmented gather matrix-vector (SGMV) kernels for batches
+ * that mix adapters.  With several LoRAs stacked, each one contributes its
+ * own alongside product and the products add up (comparison table, stacking
+ * row); a per-slot scale plays the part of the LoRA weight that diffusion
+ * schedules vary over timesteps (same section, the paragraph on diffusion).
  *
  * For each request s, each row t of that request, and each slot k whose index
  * i = idx[s][k] is valid:

@@ -13,10 +13,10 @@
  *   A: r x d_in and B: d_out x r.
  *
  *   Same page, "Exercises" (the four-requests answer) and the self-test answer
- *   on mixing LoRAs: every request carries its own LoRA index, each request's
- *   rows get their own x A^T B^T, and results land back in the original row
- *   order; section "LoRA: merged or alongside" (comparison table, "Stacking
- *   several LoRAs"): stacked LoRAs are further alongside computations, summed.
+ *   on mixing LoRAs: each request names its own adapter, each request's rows
+ *   get their own x A^T B^T, and every result goes back to the row it came
+ *   from; section "LoRA: merged or alongside" (comparison table, stacking
+ *   row): stacked LoRAs add further computations alongside, whose results add.
  *
  *   For every request s and every row t of it, for every slot k whose index
  *   i = idx[s][k] is not -1:

@@ -4,10 +4,10 @@
 //
 // "Serving several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
 // alongside": the unmerged form adds x A^T B^T to x W^T; "Exercises" (four
-// requests): requests that share a LoRA fall into one group, "making the matrix
-// multiply larger and more efficient" -- the long groups are the ones dense
-// enough for MFMA.  Comparison table, "Stacking several LoRAs": stacked
-// adapters are summed; here the slots of a tile share one accumulator.
+// requests): requests on one adapter form one partition, whose products grow
+// with its size -- the long partitions are the ones dense enough for MFMA.
+// Comparison table, row on stacking several LoRAs: stacked adapters are
+// summed; here the slots of a tile share one accumulator.
 //
 // Layout of the work.  Wave w owns tile rows 16w .. 16w+15.
 //   Shrink (per slot): V^T[j][t] = sum_c A[j][c] x[t][c] on

@@ -1,12 +1,13 @@
 // Segment / index scheduler: groups the requests of a batch by adapter and
 // cuts every group into row tiles for the apply kernels.
 //
-// "Serving several LoRAs, ControlNet and IP-Adapter", "Exercises" (the answer
-// on four requests with four LoRAs): group the batch's activations by LoRA
-// index, let one kernel handle every group, add the results back in the
-// original order; requests that share a LoRA fall into one group, which makes
-// the product larger and denser.  "Punica: Multi-Tenant LoRA Serving"
-// (contribution 1) is the same segmented-gather idea.
+// "Serving several LoRAs, ControlNet and IP-Adapter", "Exercises" (the
+// four-request, four-LoRA answer): the batch is partitioned by adapter, each
+// partition gets its own low-rank product from a single segmented kernel, and
+// the results land back in the rows they came from; requests on one adapter
+// share a partition, so its products are bigger and use the hardware better.
+// "Punica: Multi-Tenant LoRA Serving" (contribution 1) describes the same
+// segmented-gather scheme.
 //
 // The plan is built on the device by one workgroup, so indices and offsets
 // never travel to the host.  Steps:

@@ -13,7 +13,7 @@ What pins what (pages named by title and section):
   untouched        -- slots of -1 and rows outside every request are left as they are.
   permutation      -- reordering requests (with their rows) reorders the output rows;
                       "Exercises" (four requests): results go back in the original order.
-  stacking         -- comparison table, "Stacking several LoRAs": K stacked adapters
+  stacking         -- comparison table, stacking row: K stacked adapters
                       equal one adapter of rank K*r with A's stacked by rows and B's
                       by columns.
   numpy_special    -- one request, one adapter: (x A^T) B^T by numpy matmul.
