@@ -174,6 +174,7 @@ struct Meta {
   int pos[kMetaRows][LORA_MAX_SLOTS];   // original slot index of compacted slot
   float sc[kMetaRows][LORA_MAX_SLOTS];  // scale of compacted slot
   int cum[kMetaRows + 1];               // staging of the sorted row prefix sums (MFMA tiles)
+  int rec[kRecWords];                   // staging of a VALU tile's record
 };
 constexpr size_t kMetaBytes = (sizeof(Meta) + 255) & ~size_t(255);
 
@@ -183,30 +184,36 @@ __device__ __forceinline__ int rec_pos(uint2 w, int kk) {
   return int((word >> (8 * (kk & 3))) & 0xffu);
 }
 
-// Fill the tile's rows (token index, compacted slots, scales) into LDS.  VALU
-// tiles read their record (one round of independent loads, then the scales);
-// MFMA tiles find their rows' requests by a binary search over the sorted
-// rows' prefix sums, staged in LDS with one parallel load.  Ends with a barrier.
-__device__ inline void setup_rows(const ApplyArgs &a, int4 td, const int *rec, int n_active, Meta &M) {
+// Fill the metadata of a VALU tile from its record, already in registers
+// (word `tid` of it in thread tid < kRecWords); returns the tile's rows.  Only
+// per-slot scales are read from memory.  Two barriers.
+__device__ inline int setup_from_record(const ApplyArgs &a, int word, Meta &M) {
+  const int tid = threadIdx.x;
+  if (tid < kRecWords) M.rec[tid] = word;
+  __syncthreads();
+  const int nrows = M.rec[R_NROWS], nact = M.rec[R_NACT];
+  if (tid < nrows) {
+    const int s = M.rec[R_S + tid];
+    const uint2 pw = make_uint2(uint32_t(M.rec[R_POS + 2 * tid]), uint32_t(M.rec[R_POS + 2 * tid + 1]));
+    M.t[tid] = M.rec[R_T + tid];
+    for (int kk = 0; kk < nact; ++kk) {
+      const int k = rec_pos(pw, kk);
+      M.pos[tid][kk] = k;
+      M.sc[tid][kk] = a.scale ? gload<float>(a.scale + (int64_t)s * a.K + k) : 1.0f;
+    }
+  }
+  if (tid < nact) M.a[tid] = M.rec[R_A + tid];
+  if (tid == 0) M.nact = nact;
+  __syncthreads();
+  return nrows;
+}
+
+// Fill an MFMA-sized tile's rows (token index, compacted slots, scales) into
+// LDS: the rows' requests are found by a binary search over the sorted rows'
+// prefix sums, staged in LDS with one parallel load.  Ends with a barrier.
+__device__ inline void setup_rows(const ApplyArgs &a, int4 td, int n_active, Meta &M) {
   const int tid = threadIdx.x;
   const int p0 = td.x, q0 = td.y, nrows = td.z;
-  if (rec) {
-    if (tid < nrows) {
-      const int t = gload<int>(rec + R_T + tid), s = gload<int>(rec + R_S + tid);
-      const int nact = gload<int>(rec + R_NACT);
-      const uint2 pw = gload<uint2>(rec + R_POS + 2 * tid);
-      M.t[tid] = t;
-      for (int kk = 0; kk < nact; ++kk) {
-        const int k = rec_pos(pw, kk);
-        M.pos[tid][kk] = k;
-        M.sc[tid][kk] = a.scale ? gload<float>(a.scale + (int64_t)s * a.K + k) : 1.0f;
-        if (tid == 0) M.a[kk] = gload<int>(rec + R_A + kk);
-      }
-      if (tid == 0) M.nact = nact;
-    }
-    __syncthreads();
-    return;
-  }
   // a tile's rows lie in requests q0 .. q0 + nrows - 1 (each holds >= 1 row)
   const int nq = min(nrows, n_active - q0);
   if (tid <= nq) M.cum[tid] = gload<int>(a.cumlen + q0 + tid);

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
     const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
     const int4 td = gload<int4>(a.tiles_m + tile);
     const int o_lo = chunk * a.wm, o_hi = min(a.d_out, o_lo + a.wm);
-    setup_rows(a, td, nullptr, n_active, M);
+    setup_rows(a, td, n_active, M);
     if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) mfma_tile<JT, MODE>(a, pr, td.z, o_lo, o_hi, M, stage, vpark);
   });
 }

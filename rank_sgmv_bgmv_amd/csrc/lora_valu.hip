@@ -285,19 +285,64 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   const int64_t items_v = (int64_t)n_v * a.cv;
   const int64_t items_m = a.valu_takes_m ? (int64_t)n_m * a.cm : 0;
   const int64_t per_prob = items_v + items_m;
-  walk_items(per_prob * a.n_problems, [&](int64_t item) {
-    const int p = int(item / per_prob);
-    int64_t rem = item - (int64_t)p * per_prob;
+  const int64_t n_items = per_prob * a.n_problems;
+  if (n_items <= 0) return;
+  // Work items are dealt in XCD-contiguous ranges (blockIdx % 8 is the XCD):
+  // the chunks of a tile and the neighbouring tiles of one problem share that
+  // XCD's L2; the workgroups of an XCD stride through its range.
+  const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
+  const int64_t ipx = (n_items + 7) >> 3;
+  auto item_at = [&](int64_t i) -> int64_t {
+    if (i >= ipx) return -1;
+    const int64_t it = xcd * ipx + i;
+    return it < n_items ? it : -1;
+  };
+  // What an item needs before it starts -- its problem and, for a VALU tile,
+  // its record -- is loaded one item ahead, so a workgroup's next item begins
+  // without a round trip to memory.
+  struct Ahead {
+    lora_problem pr;
+    int word;
+  };
+  auto load_ahead = [&](int64_t it, Ahead &h) {
+    const int p = int(it / per_prob);
+    const int64_t rem = it - (int64_t)p * per_prob;
+    h.pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
+    h.word = 0;
+    if (rem < items_v && threadIdx.x < kRecWords)
+      h.word = gload<int>(a.vrec + (rem / a.cv) * kRecWords + threadIdx.x);
+  };
+  int64_t i = blockIdx.x >> 3;
+  int64_t it = item_at(i);
+  if (it < 0) return;
+  Ahead cur;
+  load_ahead(it, cur);
+  while (it >= 0) {
+    const int64_t nx = item_at(i + per_xcd);
+    Ahead nxt;
+    nxt.word = 0;
+    if (nx >= 0) load_ahead(nx, nxt);
+    const int p = int(it / per_prob);
+    int64_t rem = it - (int64_t)p * per_prob;
     const bool is_m = rem >= items_v;
     if (is_m) rem -= items_v;
     const int chunks = is_m ? a.cm : a.cv, width = is_m ? a.wm : a.wv;
     const int tile = int(rem / chunks), chunk = int(rem % chunks);
-    const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
-    const int4 td = gload<int4>(is_m ? a.tiles_m + tile : a.tiles_v + tile);
     const int o_lo = chunk * width, o_hi = min(a.d_out, o_lo + width);
-    setup_rows(a, td, is_m ? nullptr : a.vrec + (int64_t)tile * kRecWords, n_active, M);
-    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) valu_tile<T, VEC, MODE>(a, pr, td.z, o_lo, o_hi, M, s_v);
-  });
+    int nrows;
+    if (is_m) {
+      const int4 td = gload<int4>(a.tiles_m + tile);
+      setup_rows(a, td, n_active, M);
+      nrows = td.z;
+    } else {
+      nrows = setup_from_record(a, cur.word, M);
+    }
+    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) valu_tile<T, VEC, MODE>(a, cur.pr, nrows, o_lo, o_hi, M, s_v);
+    __syncthreads();
+    it = nx;
+    i += per_xcd;
+    cur = nxt;
+  }
 }
 
 // Launch one instantiation; the first launch lifts its dynamic-LDS limit to
