@@ -49,7 +49,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # those sources change.
 TRAFFIC_SOURCES = ["rank_sgmv_bgmv_amd/csrc/lora_valu.hip", "rank_sgmv_bgmv_amd/csrc/lora_device.hpp",
                    "rank_sgmv_bgmv_amd/csrc/lora_internal.hpp"]
-MEASURED_TRAFFIC = {"sources_sha256_16": "b78310c3b0f1c19a", "fetch_kib": 181122.0, "write_kib": 16384.0,
+MEASURED_TRAFFIC = {"sources_sha256_16": "4a73a924a5ca0da7", "fetch_kib": 181079.0, "write_kib": 16384.0,
                     "fetch_scale": 2.0, "write_scale": 1.0}
 
 
