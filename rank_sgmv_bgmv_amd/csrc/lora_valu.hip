@@ -41,8 +41,8 @@ using InterT = typename std::conditional<MODE == MODE_FUSED && VEC && sizeof(T) 
 // l+64, ...), UB pieces per lane per round for x and A each, so a round keeps
 // UB*(MB+4) independent 16-byte loads in flight per lane.  Loads use clamped
 // (always valid) addresses; pieces past the end are masked to zero.  The MB*4
-// partial sums per lane are reduced over the wave by wave_sum_scatter; no LDS
-// traffic and no barrier inside.
+// partial sums per lane are reduced over the wave by wave_sum_scatter (row by
+// row); no LDS traffic and no barrier inside.
 template <typename T, bool VEC, int MB, int MODE>
 __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
                             InterT<T, VEC, MODE> *s_v) {
@@ -88,10 +88,16 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
 #pragma unroll
             for (int i = 0; i < kJPW; ++i) acc[m * kJPW + i] = O::dot(xv[u][m], av[u][i], acc[m * kJPW + i]);
       }
-      const float val = wave_sum_scatter<NV>(acc);
-      if (lane < NV) {
-        const int m = lane / kJPW, j = j0 + lane % kJPW;
-        if (m < nb && j < r) {
+      // one reduction per row, so a row's sums do not depend on which other
+      // rows share its tile (the plan's order inside an adapter group is not fixed)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        float part[kJPW];
+#pragma unroll
+        for (int i = 0; i < kJPW; ++i) part[i] = acc[m * kJPW + i];
+        const float val = wave_sum_scatter<kJPW>(part);
+        const int j = j0 + lane;
+        if (lane < kJPW && m < nb && j < r) {
           const float vs = val * M.sc[m0 + m][kk];
           if constexpr (MODE == MODE_SHRINK)
             gstore(a.v + (int64_t)M.t[m0 + m] * a.ldv + (int64_t)M.pos[m0 + m][kk] * r + j, vs);

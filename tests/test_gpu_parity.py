@@ -300,6 +300,21 @@ def test_permutation_equivariance_bitwise(orc):
     assert np.array_equal(o2, o1[rows])
 
 
+@pytest.mark.parametrize("name", ["bf16_decode_r16", "bf16_hot_per_token_mfma"])
+def test_per_token_permutation_bitwise(orc, name):
+    """Shuffling the rows of a decode batch regroups them into different tiles;
+    each row's result must not change by a single bit."""
+    case = _rand(5005, **GRID[name])
+    b = case.batch
+    assert b.seg_off is None
+    perm = np.random.default_rng(2).permutation(b.T)
+    b2 = W.Batch(b.T, b.S, b.K, None, b.idx[perm].copy(), None if b.scale is None else b.scale[perm].copy())
+    c2 = W.Case("perm", case.dtype, b2, case.pool, case.x[perm].copy(), case.y[perm].copy())
+    o1 = DevCase(case).apply()
+    o2 = DevCase(c2).apply()
+    assert np.array_equal(o2, o1[perm])
+
+
 def test_invalid_indices_are_skipped_and_counted(orc):
     case = _rand(5003, dtype=W.BF16, n=5, r=16, d_in=64, d_out=64, S=12, K=2, min_len=1, max_len=10,
                  p_invalid=0.25, p_empty=0.2)
