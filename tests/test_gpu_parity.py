@@ -194,6 +194,55 @@ def test_c5_diffusion_sampled(orc, d, r):
     assert_parity(case, out, y_ref, touched, rows=rows, what=case.name)
 
 
+def test_decode_x32_multi_sampled(orc):
+    """The decode launch as it is timed: the 64-token Zipf batch through 32
+    q_proj pools (1000 rank-16 adapters of 4096x4096 each) in one multi-problem
+    launch sharing one plan.  Launched twice from the same y: the second launch
+    must reproduce the first bit for bit (no row's sums depend on which
+    workgroup ran it, or when).  Four layers are checked against the oracle in
+    full."""
+    layers, n, r, d = 32, 1000, 16, 4096
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(W.SEEDS["C2"])
+    batch = W.batch_c2(np.random.default_rng(W.SEEDS["C2"]), n)
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(shape, generator=gen, device=DEV) * std).to(torch.bfloat16)
+
+    pools = [(rnd(n, r, d, std=0.02), rnd(n, d, r, std=0.02)) for _ in range(layers)]
+    xs = [rnd(64, d) for _ in range(layers)]
+    y0 = [rnd(64, d) for _ in range(layers)]
+    ys = [y.clone() for y in y0]
+    db = dev_batch(batch)
+    plan = L.new_workspace(db, n, DEV)
+    L.lora_plan_build(db, n, plan)
+    table, aligned = L.problems_table([(A, B, x, y) for (A, B), x, y in zip(pools, xs, ys)], DEV)
+    assert aligned
+    shape = L.Pool(*pools[0])
+    L.lora_apply_multi(shape, db, plan, table, aligned)
+    torch.cuda.synchronize()
+    first = [y.clone() for y in ys]
+    for y, y_init in zip(ys, y0):
+        y.copy_(y_init)
+    L.lora_apply_multi(shape, db, plan, table, aligned)
+    torch.cuda.synchronize()
+    for li in range(layers):
+        assert torch.equal(ys[li].view(torch.int16), first[li].view(torch.int16)), f"layer {li}"
+    used = np.unique(batch.idx[batch.idx >= 0])
+    remap = np.full(n, -1, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    idx_small = np.where(batch.idx >= 0, remap[np.maximum(batch.idx, 0)], -1).astype(np.int32)
+    sel = torch.from_numpy(used.astype(np.int64)).to(DEV)
+    for li in (0, 9, 20, 31):
+        A_s, B_s = from_dev(pools[li][0][sel], W.BF16), from_dev(pools[li][1][sel], W.BF16)
+        pool = W.Pool(W.BF16, len(used), r, d, d, A_s, B_s)
+        small = W.Batch(64, 64, 1, None, idx_small, None)
+        case = W.Case(f"decode_x32_layer{li}", W.BF16, small, pool, from_dev(xs[li], W.BF16),
+                      from_dev(y0[li], W.BF16))
+        y_ref, touched, _, _ = orc.apply_case(case)
+        assert_parity(case, from_dev(ys[li], W.BF16), y_ref, touched, what=case.name)
+
+
 def _c4_layer(layer_seed=0):
     """One layer of the Llama-3-8B-shaped stack: the batch (shared) and 7 projection cases."""
     rng = np.random.default_rng(W.SEEDS["C4"])
