@@ -23,8 +23,10 @@
 //   Expand: Y^T[o][t] += sum_j B[o][j] v[t][j] per stage of 128 outputs (and
 //     per slot).  B is staged through LDS with the next stage prefetched into
 //     registers; y is read one stage ahead straight into the accumulator
-//     layout (8-byte pieces: lane (t, q) holds y[t][o + 4q .. +3]), added
-//     and rounded once to bf16, and written back.
+//     layout, added and rounded once to bf16, and written back.  The B rows
+//     of each pair of 16-wide output tiles are interleaved as they are staged
+//     so that a lane's two accumulators hold 8 consecutive outputs of its
+//     row: y moves in 16-byte pieces.
 // Every bf16 product is exact in fp32 and accumulation is fp32; the rank-r
 // intermediate is rounded once to bf16 before the expand.
 
@@ -165,8 +167,8 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   // stages are (output block ob, slot kk), slot-minor
   const int n_ob = (o_hi - o_lo + NO - 1) / NO;
   const int n_st = n_ob * nact;
-  uint4 br[NBV];                 // next B stage (cooperative)
-  uint2 yc[OT], yn[OT];          // y pieces of the current / next output block
+  uint4 br[NBV];                     // next B stage (cooperative)
+  uint4 yc[OT / 2], yn[OT / 2];      // y pieces of the current / next output block
   f32x4 yacc[OT];
   auto load_b = [&](int st) {
     const int ob = o_lo + (st / nact) * NO, kk = st % nact;
@@ -178,11 +180,11 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
       br[i] = ob + row < o_hi ? gload<uint4>(Bk + (int64_t)(ob + row) * R + c) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto load_y = [&](int ob, uint2(&yr)[OT]) {
+  auto load_y = [&](int ob, uint4(&yr)[OT / 2]) {
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot) {
-      const int o = ob + 16 * ot + 4 * kg;
-      yr[ot] = (row_ok && o < o_hi) ? gload<uint2>(yrow + o) : make_uint2(0, 0);
+    for (int p = 0; p < OT / 2; ++p) {
+      const int o = ob + 32 * p + 8 * kg;
+      yr[p] = (row_ok && o < o_hi) ? gload<uint4>(yrow + o) : make_uint4(0, 0, 0, 0);
     }
   };
   if (n_st > 0) {
@@ -194,10 +196,17 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   for (int st = 0; st < n_st; ++st) {
     const int ob = o_lo + (st / nact) * NO, kk = st % nact;
     __syncthreads();  // every wave is done reading the previous stage
+    // block row o' = 32p + 8a + 4h + b goes to LDS row 32p + 16h + 4a + b:
+    // output tile 2p + h then reads its rows 16(2p+h) .. +15 in order (no bank
+    // conflicts), and its row 4a + b holds output 32p + 8a + 4h + b, so that
+    // the accumulators of tiles 2p and 2p+1 give each lane 8 consecutive
+    // outputs of its row (one 16-byte y piece)
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
       const int e = tid + i * kThreads;
-      *reinterpret_cast<uint4 *>(stage + (e / (R / 8)) * BST + 8 * (e % (R / 8))) = br[i];
+      const int row = e / (R / 8);
+      const int lrow = (row & ~31) | (((row >> 2) & 1) << 4) | (((row >> 3) & 3) << 2) | (row & 3);
+      *reinterpret_cast<uint4 *>(stage + lrow * BST + 8 * (e % (R / 8))) = br[i];
     }
     __syncthreads();
     if (st + 1 < n_st) {
@@ -220,16 +229,20 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
     if (kk == nact - 1) {
       // output block done: y += delta, rounded once, written back
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot) {
-        const int o = ob + 16 * ot + 4 * kg;
+      for (int p = 0; p < OT / 2; ++p) {
+        const int o = ob + 32 * p + 8 * kg;
         if (row_ok && o < o_hi) {
-          const uint2 y0 = yc[ot];
-          gstore(yrow + o, make_uint2(pack_bf2(bf_lo(y0.x) + yacc[ot][0], bf_hi(y0.x) + yacc[ot][1]),
-                                      pack_bf2(bf_lo(y0.y) + yacc[ot][2], bf_hi(y0.y) + yacc[ot][3])));
+          const uint4 y0 = yc[p];
+          const f32x4 lo = yacc[2 * p], hi = yacc[2 * p + 1];
+          gstore(yrow + o, make_uint4(pack_bf2(bf_lo(y0.x) + lo[0], bf_hi(y0.x) + lo[1]),
+                                      pack_bf2(bf_lo(y0.y) + lo[2], bf_hi(y0.y) + lo[3]),
+                                      pack_bf2(bf_lo(y0.z) + hi[0], bf_hi(y0.z) + hi[1]),
+                                      pack_bf2(bf_lo(y0.w) + hi[2], bf_hi(y0.w) + hi[3])));
         }
-        yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
-        yc[ot] = yn[ot];
+        yc[p] = yn[p];
       }
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
