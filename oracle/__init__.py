@@ -12,9 +12,12 @@ Functions and the passages they follow (pages named by title and section):
     original order); stacked LoRAs summed (comparison table, "Stacking").
   * ``shrink`` -- the x A^T half of the same formula, per slot, scale folded in.
   * ``expand`` -- the (.) B^T half, given the float32 intermediate.
+  * ``merge``  -- same section: the merged form W + BA computed ahead of time,
+    stacked LoRAs as a weighted sum (comparison table, "Stacking"); alpha = -1
+    unmerges.
 
 Pins (tests/test_oracle_pins.py) tie every function to something other than
-itself; none of the three is "parity unpinned".
+itself; none of the four is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -72,6 +75,9 @@ class Oracle:
         self.lib.oracle_expand.restype = _I
         self.lib.oracle_expand.argtypes = [_I, _I, _I, _I, _P, _I, _I, _P, _P, _I,
                                            _P, _L, _P, _L, _P, _I, _P, _P, _I]
+        self.lib.oracle_merge.restype = _I
+        self.lib.oracle_merge.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _L, _I, _P, _P,
+                                          ctypes.c_double, _I, _I, _P, _I]
 
     @staticmethod
     def _check(rc: int):
@@ -140,6 +146,22 @@ class Oracle:
                                     _ptr(y_ref), _ptr(touched), nthreads)
         self._check(rc)
         return y_ref, touched.astype(bool)
+
+    def merge(self, dtype, A, B, W, idx, scale=None, alpha=1.0, rows=None, nthreads=0):
+        """W [d_out][ldw] encoded; idx [K] adapter indices (-1 skipped); scale [K] or None.
+        Returns W_out [row_hi - row_lo][d_in] float64 for rows = (row_lo, row_hi) (all rows by default)."""
+        n, r, d_in = A.shape
+        d_out = B.shape[1]
+        assert B.shape == (n, d_out, r) and W.shape[0] == d_out
+        A = np.ascontiguousarray(A); B = np.ascontiguousarray(B); W = np.ascontiguousarray(W)
+        idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(-1)
+        sc = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32).reshape(-1)
+        lo, hi = (0, d_out) if rows is None else rows
+        out = np.empty((hi - lo, d_in), np.float64)
+        rc = self.lib.oracle_merge(DTYPE_CODE[dtype], n, r, d_in, d_out, _ptr(A), _ptr(B), _ptr(W), W.shape[1],
+                                   int(idx.size), _ptr(idx), _ptr(sc), float(alpha), lo, hi, _ptr(out), nthreads)
+        self._check(rc)
+        return out
 
     # convenience over workloads.Case -------------------------------------
     def apply_case(self, case, rows=None, nthreads=0):

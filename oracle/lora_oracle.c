@@ -261,3 +261,46 @@ int oracle_expand(int dtype, int n, int r, int d_out, const void *B,
     free(owner);
     return OR_OK;
 }
+
+/*
+ * Merge / unmerge ("Serving several LoRAs, ControlNet and IP-Adapter", section
+ * "LoRA: merged or alongside"): the merged form computes W + BA ahead of time;
+ * stacked LoRAs merge as a weighted sum (comparison table, stacking row);
+ * unmerging subtracts what was added.  Here, for output rows o in
+ * [row_lo, row_hi) and every column c < d_in:
+ *
+ *   W_out[o - row_lo][c] = W[o][c]
+ *       + alpha * sum_k scale[k] * sum_j B[idx[k]][o][j] * A[idx[k]][j][c]
+ *
+ * over the slots k with idx[k] != -1 (j ascending, then k ascending), with
+ * scale NULL meaning 1.  alpha = 1 merges, alpha = -1 unmerges.  W is
+ * [d_out][ldw] in the pool's type; W_out is double.
+ */
+int oracle_merge(int dtype, int n, int r, int d_in, int d_out, const void *A, const void *B,
+                 const void *W, int64_t ldw, int K, const int32_t *idx, const float *scale, double alpha,
+                 int row_lo, int row_hi, double *W_out, int nthreads) {
+    if (n < 1 || r < 1 || d_in < 1 || d_out < 1 || ldw < d_in || K < 0) return OR_ESHAPE;
+    if (row_lo < 0 || row_hi > d_out || row_lo > row_hi) return OR_ESHAPE;
+    for (int k = 0; k < K; ++k)
+        if (idx[k] < -1 || idx[k] >= n) return OR_EINDEX;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4)
+#endif
+    for (int o = row_lo; o < row_hi; ++o) {
+        for (int c = 0; c < d_in; ++c) {
+            double delta = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const int i = idx[k];
+                if (i == -1) continue;
+                double sum = 0.0;
+                for (int j = 0; j < r; ++j)
+                    sum += elem(B, dtype, ((int64_t)i * d_out + o) * r + j) *
+                           elem(A, dtype, ((int64_t)i * r + j) * d_in + c);
+                delta += (scale ? (double)scale[k] : 1.0) * sum;
+            }
+            W_out[(int64_t)(o - row_lo) * d_in + c] = elem(W, dtype, (int64_t)o * ldw + c) + alpha * delta;
+        }
+    }
+    return OR_OK;
+}

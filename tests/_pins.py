@@ -21,6 +21,14 @@ What pins what (pages named by title and section):
   macs_formula     -- the multiply-adds performed match the page's lora_costs count
                       2 N (d r + r d) (section "LoRA: merged or alongside").
   shrink_numpy, expand_numpy, shrink_expand_compose -- the two halves.
+  merge_vs_unmerged -- "LoRA: merged or alongside": with K stacked slots,
+                      x W'^T - x W^T for the merged W' equals the unmerged
+                      delta of the apply oracle (a different association;
+                      non-square shapes catch transposes).
+  merge_rank1      -- r = 1: W' = W + alpha s b a^T, exact on small integers.
+  merge_inverse    -- unmerging (alpha = -1) what was merged gives W back
+                      exactly on small integers; rows subsets agree.
+  merge_numpy      -- W + alpha sum_k s_k B_k A_k by numpy matmul; -1 slots skipped.
 """
 from __future__ import annotations
 
@@ -311,9 +319,74 @@ def pin_shrink_expand_compose(orc):
     assert np.array_equal(y1, y2)
 
 
+def pin_merge_vs_unmerged(orc):
+    rng = _rng(31)
+    n, r, d_in, d_out, T = 4, 3, 6, 5, 7
+    slots = np.array([2, -1, 0], np.int32)
+    sc = _f32([1.5, 4.0, -0.75])
+    A = _f32(rng.standard_normal((n, r, d_in)))
+    B = _f32(rng.standard_normal((n, d_out, r)))
+    Wm = _f32(rng.standard_normal((d_out, d_in)))
+    x = _f32(rng.standard_normal((T, d_in)))
+    merged = orc.merge(F32, A, B, Wm, slots, sc, alpha=1.0)
+    # one request covering every row, the same slots
+    y0 = np.zeros((T, d_out), np.float32)
+    seg = np.array([0, T], np.int32)
+    y_ref, touched, _, _ = orc.apply(F32, A, B, x, y0, T=T, S=1, K=3, seg_off=seg, idx=slots[None, :],
+                                     scale=sc[None, :])
+    assert touched.all()
+    xd = x.astype(np.float64)
+    want = xd @ merged.T - xd @ Wm.astype(np.float64).T
+    assert np.allclose(y_ref, want, rtol=1e-11, atol=1e-11)
+
+
+def pin_merge_rank1(orc):
+    rng = _rng(32)
+    n, d_in, d_out = 3, 7, 4
+    A = _f32(rng.integers(-3, 4, (n, 1, d_in)))
+    B = _f32(rng.integers(-3, 4, (n, d_out, 1)))
+    Wm = _f32(rng.integers(-9, 10, (d_out, d_in)))
+    for alpha, i, s in [(1.0, 1, 2.0), (-1.0, 2, 0.5), (1.0, 0, -3.0)]:
+        got = orc.merge(F32, A, B, Wm, np.array([i], np.int32), _f32([s]), alpha=alpha)
+        for o in range(d_out):
+            for c in range(d_in):
+                want = float(Wm[o, c]) + alpha * s * float(B[i, o, 0]) * float(A[i, 0, c])
+                assert got[o, c] == want, (o, c, got[o, c], want)
+
+
+def pin_merge_inverse(orc):
+    rng = _rng(33)
+    n, r, d_in, d_out = 3, 4, 9, 6
+    A = _f32(rng.integers(-2, 3, (n, r, d_in)))
+    B = _f32(rng.integers(-2, 3, (n, d_out, r)))
+    Wm = _f32(rng.integers(-20, 21, (d_out, d_in)))
+    slots, sc = np.array([1, 2], np.int32), _f32([2.0, -1.0])
+    merged = orc.merge(F32, A, B, Wm, slots, sc, alpha=1.0)
+    assert not np.array_equal(merged, Wm.astype(np.float64))
+    back = orc.merge(F32, A, B, _f32(merged), slots, sc, alpha=-1.0)
+    assert np.array_equal(back, Wm.astype(np.float64))
+    part = orc.merge(F32, A, B, Wm, slots, sc, alpha=1.0, rows=(2, 5))
+    assert np.array_equal(part, merged[2:5])
+
+
+def pin_merge_numpy(orc):
+    rng = _rng(34)
+    n, r, d_in, d_out = 5, 6, 10, 8
+    A = _f32(rng.standard_normal((n, r, d_in)))
+    B = _f32(rng.standard_normal((n, d_out, r)))
+    Wm = _f32(rng.standard_normal((d_out, d_in + 3)))  # ld > d_in
+    slots, sc = np.array([4, -1, 1, 3], np.int32), _f32([0.5, 9.0, -2.0, 1.25])
+    got = orc.merge(F32, A, B, Wm, slots, sc, alpha=-1.0)
+    want = Wm[:, :d_in].astype(np.float64).copy()
+    for i, s in zip(slots, sc):
+        if i >= 0:
+            want -= float(s) * (B[i].astype(np.float64) @ A[i].astype(np.float64))
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [pin_merged_form, pin_rank1_closed, pin_linearity, pin_untouched, pin_permutation, pin_stacking,
             pin_numpy_special, pin_exact_bruteforce, pin_macs_formula, pin_shrink_numpy, pin_expand_numpy,
-            pin_shrink_expand_compose]
+            pin_shrink_expand_compose, pin_merge_vs_unmerged, pin_merge_rank1, pin_merge_inverse, pin_merge_numpy]
 
 
 def run_all(orc):

@@ -28,6 +28,13 @@ MUTANTS = {
     "row_uses_request": ("elem(x, dtype, (int64_t)t * ldx + c) *\n                               elem(A", "elem(x, dtype, (int64_t)s * ldx + c) *\n                               elem(A", 1),
     "shrink_drops_scale": ("vk[j] = sc * sum;", "vk[j] = sum;", 1),
     "expand_slot_offset": ("(int64_t)k * r + j] *", "(int64_t)k + j] *", 1),
+    "merge_transposed_A": ("elem(A, dtype, ((int64_t)i * r + j) * d_in + c);\n                delta",
+                           "elem(A, dtype, ((int64_t)i * d_in + c) * r + j);\n                delta", 1),
+    "merge_drops_scale": ("delta += (scale ? (double)scale[k] : 1.0) * sum;", "delta += sum;", 1),
+    "merge_ignores_alpha": ("+ alpha * delta;", "+ delta;", 1),
+    "merge_uses_minus1": ("if (i == -1) continue;\n                double sum", "if (i == -1) i = 0;\n                double sum", 1),
+    "merge_first_slot_only": ("for (int k = 0; k < K; ++k) {\n                const int i = idx[k];",
+                              "for (int k = 0; k < 1; ++k) {\n                const int i = idx[k];", 1),
 }
 
 RUNNER = r"""
