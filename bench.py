@@ -256,6 +256,46 @@ def bench_c4_stack(dev, steps, warmup, seed=W.SEEDS["C4"]):
                   {"distinct_adapters": distinct, "note": "apply_* covers the 4 multi-problem launches together"})
 
 
+def bench_merge_flux(dev, steps, warmup, r=64, layers=57, per_layer=4, d=3072):
+    """Merge one rank-r adapter into every attention projection of a FLUX-sized
+    model (57 layers x 4 projections of 3072 x 3072, bf16) with one
+    lora_merge_multi launch: the page's merge cost model, one read and one write
+    of the affected weights.  Alternate steps merge (alpha 1) and unmerge
+    (alpha -1), so the weights stay bounded."""
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(106)
+    mats = []
+    for _ in range(layers * per_layer):
+        A, B = randn_pool(gen, 1, r, d, d, dev)
+        Wm = (torch.randn((d, d), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        mats.append((A, B, Wm))
+    table, aligned = L.merge_table(mats, dev)
+    assert aligned
+    shape = L.Pool(mats[0][0], mats[0][1])
+    torch.cuda.synchronize()
+
+    def step(i, ev):
+        alpha = 1.0 if i % 2 == 0 else -1.0
+        if ev: ev[0].record()
+        L.lora_merge_multi(shape, [0], table, aligned, None, alpha)
+        if ev: ev[1].record()
+
+    wall, k_ms, _ = Timer(steps).run(step, warmup)
+    n = layers * per_layer
+    weight_bytes = n * d * d * 2
+    k_bytes = 2 * weight_bytes + n * accounting.adapter_bytes(r, d, d, 2)
+    flops = n * 2 * d * d * r
+    _, page_ms, _ = accounting.lora_costs(d, layers, per_layer, r, 4608)
+    return {"workload": f"merge r{r} into {n} projections of {d}x{d} bf16 (FLUX-sized)",
+            "ms_per_step": round(wall / steps * 1e3, 5), "merge_ms": round(k_ms, 4),
+            "launches_per_step": 1, "bytes_per_step": k_bytes, "GBps": k_bytes / (k_ms * 1e-3) / 1e9,
+            "frac_hbm": k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "TFLOPs": flops / (k_ms * 1e-3) / 1e12,
+            "roof_ms_at_8TBps": round(k_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+            "page_model_ms_at_3350GBps": round(page_ms, 3)}
+
+
 # -------------------------------------------------------------- cpu baseline --
 def cpu_baseline_decode(state, layers_sample=8, min_seconds=12.0):
     """The fp64 oracle on the host for the headline workload: one 64-token
@@ -319,7 +359,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5")
+    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5,merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
@@ -358,6 +398,10 @@ def main():
             log(f"c5 d{d} r{r} ...")
             variants[f"C5_d{d}_r{r}"] = bench_single(W.case_c5(d, r), dev, args.steps, args.warmup,
                                                      f"C5 diffusion d{d} r{r}")
+    if want("merge"):
+        log("merge ...")
+        torch.cuda.empty_cache()
+        variants["merge_flux_r64"] = bench_merge_flux(dev, max(6, args.steps // 5), max(2, args.warmup // 5))
     if want("c4"):
         log("c4 ...")
         torch.cuda.empty_cache()
@@ -372,7 +416,7 @@ def main():
         name, head = next(iter(variants.items()))
     line = {
         "metric": "LoRA-delta tokens/s + achieved HBM GB/s (% of peak), decode & prefill SGMV",
-        "value": head["tokens_per_s"],
+        "value": head.get("tokens_per_s"),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -387,11 +431,11 @@ def main():
                                                   "adapters per layer, 4096->4096 bf16, plan + one fused multi-layer "
                                                   "launch per step", "global_batch": 64, "seq_len": 1,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": head["apply_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["apply_GBps"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": head.get("apply_GBps", head.get("GBps")), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head.get("apply_GBps", head.get("GBps")) / HBM_PEAK_GBS,
                      "traffic": measured_traffic_bytes() if head is not None and "decode" in head["workload"] else None,
                      "kernel": "valu_kernel<bf16, vec, fused> (shrink + expand of every decode tile, one launch for all 32 layers)",
-                     "bytes_per_launch": head["apply_bytes_per_launch"], "avg_launch_us": head["apply_kernel_us"]},
+                     "bytes_per_launch": head.get("apply_bytes_per_launch"), "avg_launch_us": head.get("apply_kernel_us")},
         "cpu_baseline": cpu,
         "headline": head,
         "variants": variants,

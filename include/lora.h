@@ -168,6 +168,52 @@ lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, co
                              int32_t n_problems, const lora_problem *problems, int32_t problems_aligned,
                              hipStream_t stream);
 
+/* Merge stacked adapters into a weight, or unmerge them, in place ("Serving
+ * several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
+ * alongside": the merged form adds BA into W ahead of time; stacked LoRAs
+ * merge as a weighted sum, comparison table, stacking row; switching
+ * unmerges the old adapter and merges the new one):
+ *
+ *     W[o][c] += alpha * sum_k scale[k] * sum_j B_{idx[k]}[o][j] * A_{idx[k]}[j][c]
+ *
+ * for every o < d_out and c < d_in, accumulated in fp32 and rounded once
+ * (round-to-nearest-even) to W's type.  alpha = 1 merges, alpha = -1
+ * unmerges; in bf16 a merge followed by an unmerge returns W up to one
+ * rounding of each step.
+ *   idx    HOST [n_slots] adapter indices, 1 <= n_slots <= LORA_MAX_SLOTS;
+ *          -1 skips the slot, any other value outside [0, n_adapters) is
+ *          rejected (LORA_EINVAL) and nothing is launched.
+ *   scale  HOST [n_slots] per-slot weights, or NULL for 1.0.
+ *   W      DEVICE [d_out][ldw], the pool's dtype, ldw >= d_in; must not
+ *          overlap the pool.
+ * Asynchronous on `stream`; allocates nothing.  Every element of W is read
+ * and written once: the bound is 2 * d_out * d_in * sizeof(element) bytes of
+ * HBM traffic. */
+lora_status lora_merge(const lora_pool *pool, const int32_t *idx, const float *scale, int32_t n_slots, float alpha,
+                       void *W, int64_t ldw, hipStream_t stream);
+
+/* One weight of a lora_merge_multi launch: its adapter pool (same shape for
+ * every problem) and the weight.  The array of these lives in DEVICE memory. */
+typedef struct {
+  const void *A;  /* [n][rank][d_in]  */
+  const void *B;  /* [n][d_out][rank] */
+  void *W;        /* [d_out][ldw], updated in place */
+  int64_t ldw;
+} lora_merge_problem;
+
+/* lora_merge for n_problems weights of one shape in ONE launch: for each
+ * entry of `problems` (a DEVICE array), W += alpha * sum_k scale[k] B_i A_i
+ * with i = idx[k] taken from that entry's pool.  `shape` gives rank, d_in,
+ * d_out, n_adapters and dtype (its A and B are ignored); idx and scale are
+ * HOST arrays as for lora_merge and apply to every problem.  The library
+ * cannot check the pointers inside the device array: the weights must not
+ * overlap one another or any pool, ldw >= d_in, and the matrix-core path
+ * (bf16) is taken only when `problems_aligned` is 1, which promises 16-byte
+ * aligned A, B and W and ldw a multiple of 8. */
+lora_status lora_merge_multi(const lora_pool *shape, const int32_t *idx, const float *scale, int32_t n_slots,
+                             float alpha, int32_t n_problems, const lora_merge_problem *problems,
+                             int32_t problems_aligned, hipStream_t stream);
+
 /* Synchronizes `stream` and stores in *count the number of invalid adapter
  * indices and segment-offset violations the last plan build met. */
 lora_status lora_read_device_errors(const void *plan, size_t plan_bytes, int32_t *count, hipStream_t stream);

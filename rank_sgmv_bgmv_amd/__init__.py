@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
             "lora_expand_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
             "lora_apply_multi": (ctypes.c_int, [pp, pb, P, SZ, I32, P, I32, P]),
             "lora_read_device_errors": (ctypes.c_int, [P, SZ, ctypes.POINTER(I32), P]),
+            "lora_merge": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, P, I64, P]),
+            "lora_merge_multi": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, I32, P, I32, P]),
             "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "lora_abi_version": (I32, []),
         }
@@ -228,6 +230,42 @@ def lora_apply_multi(shape: Pool, batch: Batch, plan, table, aligned: bool = Tru
     n = int(table.shape[0]) if table.numel() else 0
     _check(lib().lora_apply_multi(ctypes.byref(shape.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), n,
                                   _ptr(table), 1 if aligned else 0, _stream(plan)), "lora_apply_multi")
+
+
+def lora_merge(pool: Pool, idx: Sequence[int], W, scale: Optional[Sequence[float]] = None, alpha: float = 1.0):
+    """W += alpha * sum_k scale[k] B_idx[k] A_idx[k] in place (alpha = -1 unmerges).
+    idx and scale are host sequences; W is a [d_out][ldw] device tensor of the pool's dtype."""
+    if W.dim() != 2 or W.shape[0] != pool.d_out or W.shape[1] < pool.d_in or W.dtype != pool.A.dtype:
+        raise LoraError(-2, "W must be [d_out][>= d_in] with the pool's dtype")
+    ids = (ctypes.c_int32 * len(idx))(*[int(i) for i in idx])
+    sc = None if scale is None else (ctypes.c_float * len(scale))(*[float(v) for v in scale])
+    _check(lib().lora_merge(ctypes.byref(pool.c), ids, sc, len(idx), float(alpha), _ptr(W), _ld(W), _stream(W)),
+           "lora_merge")
+
+
+def merge_table(problems: Sequence, device):
+    """Device array of lora_merge_problem for (A, B, W) tuples of one shape;
+    returns (table tensor, all_aligned).  The tensors must stay alive while it is used."""
+    torch = _torch()
+    rows, aligned = [], True
+    for A, B, W in problems:
+        e = 8 if A.dtype == torch.bfloat16 else 4
+        ldw = _ld(W)
+        ptrs = [_ptr(A), _ptr(B), _ptr(W)]
+        aligned &= all(p % 16 == 0 for p in ptrs) and ldw % e == 0
+        rows.append(ptrs + [ldw])
+    table = torch.tensor(rows, dtype=torch.int64).to(device)
+    return table, aligned
+
+
+def lora_merge_multi(shape: Pool, idx: Sequence[int], table, aligned: bool = True,
+                     scale: Optional[Sequence[float]] = None, alpha: float = 1.0):
+    """lora_merge over every (A, B, W) of a merge_table in one launch."""
+    ids = (ctypes.c_int32 * len(idx))(*[int(i) for i in idx])
+    sc = None if scale is None else (ctypes.c_float * len(scale))(*[float(v) for v in scale])
+    n = int(table.shape[0]) if table.numel() else 0
+    _check(lib().lora_merge_multi(ctypes.byref(shape.c), ids, sc, len(idx), float(alpha), n, _ptr(table),
+                                  1 if aligned else 0, _stream(table)), "lora_merge_multi")
 
 
 def lora_read_device_errors(plan) -> int:

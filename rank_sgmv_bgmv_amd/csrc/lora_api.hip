@@ -239,7 +239,7 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
 
 extern "C" {
 
-int32_t lora_abi_version(void) { return 100; }
+int32_t lora_abi_version(void) { return 101; }
 
 const char *lora_status_string(lora_status s) {
   switch (s) {
@@ -324,6 +324,68 @@ lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, co
   a.n_problems = n_problems;
   const Launch L = configure(MODE_FUSED, shape, d, P, n_problems, vec, a);
   if (launch_all(MODE_FUSED, shape->dtype, L, a, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
+// Active slots of a merge (host arrays): indices and alpha-folded scales.
+lora_status merge_slots(const lora_pool *shape, const int32_t *idx, const float *scale, int32_t n_slots, float alpha,
+                        MergeArgs &a) {
+  if (!idx) return LORA_EINVAL;
+  if (n_slots < 1) return LORA_ESHAPE;
+  if (n_slots > LORA_MAX_SLOTS) return LORA_EUNSUPPORTED;
+  for (int k = 0; k < n_slots; ++k) {
+    const int i = idx[k];
+    if (i == -1) continue;
+    if (i < -1 || i >= shape->n_adapters) return LORA_EINVAL;
+    a.idx[a.nslots] = i;
+    a.s[a.nslots] = alpha * (scale ? scale[k] : 1.0f);
+    ++a.nslots;
+  }
+  a.r = shape->rank;
+  a.d_in = shape->d_in;
+  a.d_out = shape->d_out;
+  a.n_strips = (shape->d_in + 127) / 128;
+  return LORA_OK;
+}
+
+lora_status lora_merge(const lora_pool *pool, const int32_t *idx, const float *scale, int32_t n_slots, float alpha,
+                       void *W, int64_t ldw, hipStream_t stream) {
+  lora_status st = check_pool(pool);
+  if (st) return st;
+  if (!W) return LORA_EINVAL;
+  if (ldw < pool->d_in) return LORA_ESHAPE;
+  const int eb = elem_bytes(pool->dtype);
+  const size_t ws = span_bytes(pool->d_out, ldw, pool->d_in, eb);
+  const size_t as = size_t(pool->n_adapters) * pool->rank * pool->d_in * eb;
+  const size_t bs = size_t(pool->n_adapters) * pool->d_out * pool->rank * eb;
+  if (overlap(W, ws, pool->A, as) || overlap(W, ws, pool->B, bs)) return LORA_EINVAL;
+  MergeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  if ((st = merge_slots(pool, idx, scale, n_slots, alpha, a))) return st;
+  if (a.nslots == 0) return LORA_OK;
+  a.single = lora_merge_problem{pool->A, pool->B, W, ldw};
+  a.n_problems = 1;
+  a.aligned = aligned16(pool->A) && aligned16(pool->B) && aligned16(W) && ldw % 8 == 0;
+  if (launch_merge(a, pool->dtype, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
+lora_status lora_merge_multi(const lora_pool *shape, const int32_t *idx, const float *scale, int32_t n_slots,
+                             float alpha, int32_t n_problems, const lora_merge_problem *problems,
+                             int32_t problems_aligned, hipStream_t stream) {
+  if (!shape) return LORA_EINVAL;
+  lora_status st = check_shape(shape);
+  if (st) return st;
+  if (n_problems < 0) return LORA_ESHAPE;
+  if (n_problems > 0 && !problems) return LORA_EINVAL;
+  MergeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  if ((st = merge_slots(shape, idx, scale, n_slots, alpha, a))) return st;
+  if (a.nslots == 0 || n_problems == 0) return LORA_OK;
+  a.probs = problems;
+  a.n_problems = n_problems;
+  a.aligned = problems_aligned ? 1 : 0;
+  if (launch_merge(a, shape->dtype, stream) != hipSuccess) return LORA_EHIP;
   return LORA_OK;
 }
 

@@ -13,22 +13,26 @@ namespace lora {
 // every LDS access would wait for all loads in flight.  Every access to
 // caller memory goes through these, as a global (address space 1) access.
 #define LORA_GLOBAL __attribute__((address_space(1)))
-// raw register types of 2 .. 16 bytes (and 48 for a lora_problem)
+// raw register types of 2 .. 16 bytes (and 32 / 48 for a lora_merge_problem / lora_problem)
 template <int N> struct Raw;
 template <> struct Raw<2> { typedef unsigned short type; };
 template <> struct Raw<4> { typedef unsigned int type; };
 template <> struct Raw<8> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
 template <> struct Raw<16> { typedef unsigned int type __attribute__((ext_vector_type(4))); };
+template <> struct Raw<32> {
+  struct type { Raw<16>::type q[2]; };
+};
 template <> struct Raw<48> {
   struct type { Raw<16>::type q[3]; };
 };
 template <typename V, typename T>
 __device__ __forceinline__ V gload(const T *p) {
   typedef typename Raw<sizeof(V)>::type R;
-  if constexpr (sizeof(V) == 48) {
+  if constexpr (sizeof(V) == 32 || sizeof(V) == 48) {
     const LORA_GLOBAL Raw<16>::type *q = (const LORA_GLOBAL Raw<16>::type *)(p);
     R r;
-    r.q[0] = q[0]; r.q[1] = q[1]; r.q[2] = q[2];
+#pragma unroll
+    for (int i = 0; i < int(sizeof(V) / 16); ++i) r.q[i] = q[i];
     return __builtin_bit_cast(V, r);
   } else {
     const R r = *(const LORA_GLOBAL R *)(p);
@@ -78,6 +82,13 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 __device__ __forceinline__ uint16_t f_to_bf(float a) { return uint16_t(pack_bf2(a, 0.f) & 0xffffu); }
+
+// v, or zeros, selected by value where the data is used (a select between
+// two vector objects would pick between their addresses and keep them in
+// memory; a select right after a load would wait for it).
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
 
 __device__ __forceinline__ float dot2_bf(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);

@@ -153,6 +153,22 @@ struct ApplyArgs {
   int valu_takes_m;  // the VALU kernel also runs the MFMA-sized tiles (no MFMA kernel launched)
 };
 
+// Merge / unmerge of stacked adapters into weights: for every problem p,
+// W_p += sum_k s[k] B_{p,idx[k]} A_{p,idx[k]} (alpha folded into s).
+struct MergeArgs {
+  lora_merge_problem single;
+  const lora_merge_problem *probs;  // device array, or nullptr => `single`
+  int n_problems;
+  int idx[LORA_MAX_SLOTS];  // active slots' adapter indices
+  float s[LORA_MAX_SLOTS];
+  int nslots;  // active slots, 1 .. LORA_MAX_SLOTS
+  int r, d_in, d_out;
+  int n_strips;  // column strips of the matrix-core path
+  int aligned;   // every problem's pointers and ldw allow 16-byte accesses
+};
+bool merge_mfma_eligible(const MergeArgs &a, int dtype);
+hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t stream);
+
 size_t valu_smem_bytes(int kr_max);
 size_t mfma_smem_bytes(int jt, int slots);
 

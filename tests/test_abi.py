@@ -40,7 +40,7 @@ def test_exported_symbols_match_binding(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lora_abi_version() == 100
+    assert lib.lora_abi_version() == 101
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.lora_status_string(st)
     assert b"workspace" in lib.lora_status_string(-3)
@@ -119,3 +119,39 @@ def test_split_and_multi_validation(lib):
     assert lib.lora_plan_build(ctypes.byref(batch), 4, FAKE * 2000, 16, None) == -3
     cnt = ctypes.c_int32(0)
     assert lib.lora_read_device_errors(None, 1 << 20, ctypes.byref(cnt), None) == -1
+
+
+def _merge(lib, pool, idx=(1,), scale=None, n_slots=None, alpha=1.0, W=FAKE * 3000, ldw=64):
+    ids = (ctypes.c_int32 * max(len(idx), 1))(*idx)
+    sc = None if scale is None else (ctypes.c_float * len(scale))(*scale)
+    n = len(idx) if n_slots is None else n_slots
+    return lib.lora_merge(ctypes.byref(pool), ids, sc, n, alpha, W, ldw, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(idx=(4,)), -1),                   # index >= n_adapters
+    (dict(idx=(0, -2)), -1),                # index below -1
+    (dict(n_slots=0), -2),
+    (dict(idx=(0,) * 9), -4),
+    (dict(ldw=63), -2),
+    (dict(W=None), -1),
+    (dict(W=FAKE + 128), -1),               # W overlaps the pool's A
+    (dict(pool=dict(B=None)), -1),
+    (dict(pool=dict(rank=300)), -4),
+    (dict(idx=(-1, -1)), 0),                # nothing to merge: returns before any launch
+])
+def test_merge_validation(lib, case, expect):
+    pool = _pool(**case.pop("pool", {}))
+    assert _merge(lib, pool, **case) == expect
+
+
+def test_merge_multi_validation(lib):
+    shape = _pool()
+    ids = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.lora_merge_multi(None, ids, None, 2, 1.0, 3, FAKE, 1, None) == -1
+    assert lib.lora_merge_multi(ctypes.byref(shape), ids, None, 2, 1.0, 3, None, 1, None) == -1
+    assert lib.lora_merge_multi(ctypes.byref(shape), ids, None, 2, 1.0, -1, FAKE, 1, None) == -2
+    assert lib.lora_merge_multi(ctypes.byref(shape), None, None, 2, 1.0, 3, FAKE, 1, None) == -1
+    bad = (ctypes.c_int32 * 2)(0, 4)
+    assert lib.lora_merge_multi(ctypes.byref(shape), bad, None, 2, 1.0, 3, FAKE, 1, None) == -1
+    assert lib.lora_merge_multi(ctypes.byref(shape), ids, None, 2, 1.0, 0, FAKE, 1, None) == 0  # nothing to do
