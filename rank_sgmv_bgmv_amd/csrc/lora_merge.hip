@@ -17,12 +17,13 @@
 // W moves in 16-byte pieces.  B rows go straight into the MFMA operand
 // registers.  Per step and slot: D^T (columns x rows) = A^T B^T on
 // v_mfma_f32_16x16x32_bf16, then total += s_k D in fp32; W + total is rounded
-// once.  W and B of the next step are loaded while the current one computes.
+// once.  W and B are loaded two steps ahead.
 //
 // fp32, and bf16 shapes the matrix-core path does not take: a VALU kernel in
 // which each thread keeps 4 consecutive columns of 16 rows in fp32.
 
 #include <algorithm>
+#include <utility>
 
 #include "lora_device.hpp"
 
@@ -32,6 +33,17 @@ namespace {
 constexpr int kStripCols = 128;  // columns of W per strip (MFMA path)
 constexpr int kStepRows = 64;    // rows per step: 16 per wave
 constexpr int kStepsPerItem = 8;
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1: ring slot indices
+// that are constant expressions, so the ring stays in registers.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ f32x4 mfma32(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -45,7 +57,9 @@ __device__ __forceinline__ int strip_row(int c) {
   return (c & ~31) | (((c >> 2) & 1) << 4) | (((c >> 3) & 3) << 2) | (c & 3);
 }
 
-template <int KSR>  // k-steps of 32 per slot (rank padded to 32 * KSR)
+// KSR: k-steps of 32 per slot (rank padded to 32 * KSR); NE >= slots * KSR:
+// B operand registers per lane and step.
+template <int KSR, int NE>
 __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t *at = reinterpret_cast<uint16_t *>(smem);  // [slot][kStripCols][RP + 8]
@@ -83,29 +97,30 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
     __syncthreads();
 
     // --- walk the rows: lane (l16, kg) of wave w owns row o = row0 + 64 step + 16 w + l16
-    //     and, in each 32-column group p, the columns 32 p + 8 kg .. +7.  The B
-    //     operands are (slot, k-step) entries, slot-major: at most 8 of them.
-    constexpr int NP = kStripCols / 32, NE = 8;
-    uint4 wc[NP], wn[NP];  // W pieces of the current / next step
-    uint4 bc[NE], bn[NE];  // B operands of the current / next step
-    auto load = [&](int step, uint4(&wr)[NP], uint4(&br)[NE]) {
+    //     and, in each 32-column group q, the columns 32 q + 8 kg .. +7.  The B
+    //     operands are (slot, k-step) entries, slot-major.  A step's W pieces and
+    //     B operands are loaded D - 1 steps ahead into a ring of registers whose
+    //     slots are fixed at compile time (no copies: copying a register whose
+    //     load is in flight would wait for it).  Steps past the end re-read the
+    //     last one (never used), so that every path issues the same loads.
+    constexpr int NP = kStripCols / 32, D = NE >= 8 ? 2 : 3;
+    uint4 wr[D][NP], br[D][NE];
+    const int n_steps = min(kStepsPerItem, (d_out - row0 + kStepRows - 1) / kStepRows);
+    auto load = [&](int step, uint4(&wv)[NP], uint4(&bv)[NE]) {
       const int o = row0 + step * kStepRows + 16 * w + l16;
       const int oc = o < d_out ? o : d_out - 1;  // rows past d_out read the last row; never stored
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
         const int c = c0 + 32 * q + 8 * kg;
-        wr[q] = gload<uint4>(W + (int64_t)oc * ldw + (c < d_in ? c : 0));
+        wv[q] = gload<uint4>(W + (int64_t)oc * ldw + (c < d_in ? c : 0));
       }
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
-        const int k = e / KSR, j = 32 * (e % KSR) + 8 * kg;
-        if (k < ns) br[e] = gload<uint4>(Bk(k) + (int64_t)oc * r + (j < r ? j : 0));
+        const int k = min(e / KSR, ns - 1), j = 32 * (e % KSR) + 8 * kg;
+        bv[e] = gload<uint4>(Bk(k) + (int64_t)oc * r + (j < r ? j : 0));
       }
     };
-    const int n_steps = min(kStepsPerItem, (d_out - row0 + kStepRows - 1) / kStepRows);
-    load(0, wc, bc);
-    for (int step = 0; step < n_steps; ++step) {
-      if (step + 1 < n_steps) load(step + 1, wn, bn);
+    auto compute = [&](int step, const uint4(&wv)[NP], const uint4(&bv)[NE]) {
       f32x4 tot[2 * NP], acc[2 * NP];
 #pragma unroll
       for (int t = 0; t < 2 * NP; ++t) tot[t] = acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -114,12 +129,12 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
         const int k = e / KSR, ks = e % KSR;
         if (k < ns) {
           // B columns past r are zero (A^T is zero there too, but B may hold anything)
-          const uint4 bv = keep_if(32 * ks + 8 * kg < r, bc[e]);
+          const uint4 b = keep_if(32 * ks + 8 * kg < r, bv[e]);
 #pragma unroll
           for (int t = 0; t < 2 * NP; ++t) {
             const uint4 av =
                 *reinterpret_cast<const uint4 *>(at + ((int64_t)k * kStripCols + 16 * t + l16) * AST + 32 * ks + 8 * kg);
-            acc[t] = mfma32(av, bv, acc[t]);
+            acc[t] = mfma32(av, b, acc[t]);
           }
           if (ks == KSR - 1) {  // the slot is complete: scale it in fp32
             const float s = a.s[k];
@@ -131,14 +146,14 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
           }
         }
       }
-      // lane: row o, columns 32 p + 8 kg + (0..3) in tot[2p], (4..7) in tot[2p+1]
+      // lane: row o, columns 32 q + 8 kg + (0..3) in tot[2q], (4..7) in tot[2q+1]
       const int o = row0 + step * kStepRows + 16 * w + l16;
       if (o < d_out) {
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
           const int c = c0 + 32 * q + 8 * kg;
           if (c < d_in) {
-            const uint4 y0 = wc[q];
+            const uint4 y0 = wv[q];
             const f32x4 lo = tot[2 * q], hi = tot[2 * q + 1];
             gstore(W + (int64_t)o * ldw + c,
                    make_uint4(pack_bf2(bf_lo(y0.x) + lo[0], bf_hi(y0.x) + lo[1]),
@@ -148,10 +163,18 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int q = 0; q < NP; ++q) wc[q] = wn[q];
-#pragma unroll
-      for (int e = 0; e < NE; ++e) bc[e] = bn[e];
+    };
+    static_for<D - 1>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      load(min(d, n_steps - 1), wr[d], br[d]);
+    });
+    for (int s0 = 0; s0 < n_steps; s0 += D) {
+      static_for<D>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        const int step = s0 + d;
+        load(min(step + D - 1, n_steps - 1), wr[(d + D - 1) % D], br[(d + D - 1) % D]);
+        if (step < n_steps) compute(step, wr[d], br[d]);
+      });
     }
   });
 }
@@ -220,14 +243,24 @@ __global__ __launch_bounds__(kThreads) void merge_valu_kernel(MergeArgs a) {
   });
 }
 
-template <int KSR>
+template <int KSR, int NE>
 hipError_t launch_mfma_ksr(const MergeArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&merge_mfma_kernel<KSR>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&merge_mfma_kernel<KSR, NE>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
-  hipLaunchKernelGGL((merge_mfma_kernel<KSR>), dim3(grid), dim3(kThreads), smem, stream, a);
+  hipLaunchKernelGGL((merge_mfma_kernel<KSR, NE>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
+}
+
+// NE: the (slot, k-step) entries, rounded up to 1, 2, 4 or 8.
+template <int KSR>
+hipError_t launch_mfma_ne(const MergeArgs &a, int grid, size_t smem, hipStream_t stream) {
+  const int ne = a.nslots * KSR;
+  if (ne <= 1 && KSR <= 1) return launch_mfma_ksr<KSR, (KSR <= 1 ? 1 : KSR)>(a, grid, smem, stream);
+  if (ne <= 2 && KSR <= 2) return launch_mfma_ksr<KSR, (KSR <= 2 ? 2 : KSR)>(a, grid, smem, stream);
+  if (ne <= 4 && KSR <= 4) return launch_mfma_ksr<KSR, (KSR <= 4 ? 4 : KSR)>(a, grid, smem, stream);
+  return launch_mfma_ksr<KSR, 8>(a, grid, smem, stream);
 }
 
 }  // namespace
@@ -246,10 +279,10 @@ hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t stream) {
     const int grid = int(std::min<int64_t>((items + 7) / 8 * 8, 2048));
     const size_t smem = size_t(a.nslots) * kStripCols * (32 * k2 + 8) * 2;
     switch (k2) {
-      case 1: return launch_mfma_ksr<1>(a, grid, smem, stream);
-      case 2: return launch_mfma_ksr<2>(a, grid, smem, stream);
-      case 4: return launch_mfma_ksr<4>(a, grid, smem, stream);
-      default: return launch_mfma_ksr<8>(a, grid, smem, stream);
+      case 1: return launch_mfma_ne<1>(a, grid, smem, stream);
+      case 2: return launch_mfma_ne<2>(a, grid, smem, stream);
+      case 4: return launch_mfma_ne<4>(a, grid, smem, stream);
+      default: return launch_mfma_ne<8>(a, grid, smem, stream);
     }
   }
   const int64_t items = (int64_t)((a.d_in + kValuCols - 1) / kValuCols) *
