@@ -296,6 +296,73 @@ def bench_merge_flux(dev, steps, warmup, r=64, layers=57, per_layer=4, d=3072):
             "page_model_ms_at_3350GBps": round(page_ms, 3)}
 
 
+def bench_pool_load(dev, reps=5, n_slots=64, r=64, d=4096, apply_reps=40):
+    """Pool slot management: 64 rank-64 adapters (4096 x 4096, bf16, 1 MiB each)
+    copied from page-locked host memory into pool slots with lora_pool_load on a
+    second stream, alone and while the compute stream runs decode applies (the
+    64-token Zipf batch through one 1000-adapter q_proj pool) on other memory."""
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(107)
+    A = torch.zeros((n_slots, r, d), dtype=torch.bfloat16, device=dev)
+    B = torch.zeros((n_slots, d, r), dtype=torch.bfloat16, device=dev)
+    dst = L.Pool(A, B)
+    hA = torch.randn((n_slots, r, d), dtype=torch.float32).to(torch.bfloat16).pin_memory()
+    hB = torch.randn((n_slots, d, r), dtype=torch.float32).to(torch.bfloat16).pin_memory()
+    load_bytes = n_slots * accounting.adapter_bytes(r, d, d, 2)
+    # the compute job
+    cA, cB = randn_pool(gen, 1000, 16, d, d, dev)
+    pool = L.Pool(cA, cB)
+    b = W.batch_c2(np.random.default_rng(W.SEEDS["C2"]), 1000)
+    db = dev_batch(b, dev)
+    x, y = randn_act(gen, 64, d, dev), randn_act(gen, 64, d, dev)
+    plan = L.new_workspace(db, 1000, dev)
+    L.lora_plan_build(db, 1000, plan)
+    copy = torch.cuda.Stream(device=dev)  # default priority
+    compute = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def loads():
+        e0, e1 = ev(), ev()
+        e0.record(copy)
+        for i in range(n_slots):
+            L.lora_pool_load(dst, i, hA[i], hB[i], stream=copy)
+        e1.record(copy)
+        return e0, e1
+
+    def applies():
+        e0, e1 = ev(), ev()
+        e0.record(compute)
+        for _ in range(apply_reps):
+            L.lora_apply_planned(pool, db, plan, x, y)
+        e1.record(compute)
+        return e0, e1
+
+    res = {"loads_alone": [], "applies_alone": [], "loads_overlapped": [], "applies_overlapped": []}
+    for rep in range(reps + 1):
+        torch.cuda.synchronize()
+        la = loads(); torch.cuda.synchronize()
+        aa = applies(); torch.cuda.synchronize()
+        lo = loads(); ao = applies(); torch.cuda.synchronize()
+        if rep == 0:
+            continue  # warm-up
+        res["loads_alone"].append(la[0].elapsed_time(la[1]))
+        res["applies_alone"].append(aa[0].elapsed_time(aa[1]))
+        res["loads_overlapped"].append(lo[0].elapsed_time(lo[1]))
+        res["applies_overlapped"].append(ao[0].elapsed_time(ao[1]))
+    m = {k: float(np.median(v)) for k, v in res.items()}
+    return {"workload": f"load {n_slots} rank-{r} {d}x{d} bf16 adapters from pinned memory into pool slots",
+            "bytes": load_bytes, "loads_ms": round(m["loads_alone"], 4),
+            "load_GBps": load_bytes / (m["loads_alone"] * 1e-3) / 1e9,
+            "ms_per_0.1GB": round(m["loads_alone"] * 0.1e9 / load_bytes, 3),
+            "page_ms_per_0.1GB_at_25GBps": 4.0,
+            "applies_ms_alone": round(m["applies_alone"], 4),
+            "applies_ms_with_loads": round(m["applies_overlapped"], 4),
+            "loads_ms_with_applies": round(m["loads_overlapped"], 4),
+            "apply_launches": apply_reps}
+
+
 # -------------------------------------------------------------- cpu baseline --
 def cpu_baseline_decode(state, layers_sample=8, min_seconds=12.0):
     """The fp64 oracle on the host for the headline workload: one 64-token
@@ -359,7 +426,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5,merge")
+    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5,merge,poolload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
@@ -402,6 +469,9 @@ def main():
         log("merge ...")
         torch.cuda.empty_cache()
         variants["merge_flux_r64"] = bench_merge_flux(dev, max(6, args.steps // 5), max(2, args.warmup // 5))
+    if want("poolload"):
+        log("pool load ...")
+        variants["pool_load_pinned"] = bench_pool_load(dev)
     if want("c4"):
         log("c4 ...")
         torch.cuda.empty_cache()
@@ -421,7 +491,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"],
+        "ms_per_step": head.get("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -432,7 +502,7 @@ def main():
                                                   "launch per step", "global_batch": 64, "seq_len": 1,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": head.get("apply_GBps", head.get("GBps")), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": head.get("apply_GBps", head.get("GBps")) / HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": (head.get("apply_GBps", head.get("GBps")) or 0.0) / HBM_PEAK_GBS,
                      "traffic": measured_traffic_bytes() if head is not None and "decode" in head["workload"] else None,
                      "kernel": "valu_kernel<bf16, vec, fused> (shrink + expand of every decode tile, one launch for all 32 layers)",
                      "bytes_per_launch": head.get("apply_bytes_per_launch"), "avg_launch_us": head.get("apply_kernel_us")},

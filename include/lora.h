@@ -123,8 +123,12 @@ size_t lora_workspace_size(const lora_batch *batch, int32_t n_adapters);
 
 /* Build the plan for `batch` into `ws` on `stream`: sort requests by adapter
  * (the grouping of the "Exercises" answer), split groups into row tiles, and
- * record the device error word.  The batch arrays must stay unchanged until
- * every call that uses the plan has run. */
+ * record the device error word.  seg_off and idx must stay unchanged until
+ * every call that uses the plan has run.  The plan depends on them (and on T,
+ * S, K) only: scale is read by every call that uses the plan, so a per-step
+ * scale schedule ("LoRA: merged or alongside", the paragraph on diffusion:
+ * the LoRA's weight may change with the timestep) passes each step's scale
+ * array with the same plan. */
 lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *ws, size_t ws_bytes,
                             hipStream_t stream);
 
@@ -213,6 +217,23 @@ typedef struct {
 lora_status lora_merge_multi(const lora_pool *shape, const int32_t *idx, const float *scale, int32_t n_slots,
                              float alpha, int32_t n_problems, const lora_merge_problem *problems,
                              int32_t problems_aligned, hipStream_t stream);
+
+/* Copy one adapter from host memory into slot `slot` of a resident pool
+ * ("Serving several LoRAs, ControlNet and IP-Adapter", section "Placement":
+ * LoRAs stay resident; what does not stay resident is moved from page-locked
+ * host memory on demand, at PCIe speed).
+ *   A_host  HOST [rank][d_in], B_host HOST [d_out][rank], the pool's dtype,
+ *           contiguous.  Page-locked memory (hipHostMalloc, or a torch tensor
+ *           with pin_memory) makes the copy asynchronous on `stream`;
+ *           pageable memory is copied too, but the call may return only after
+ *           the host side has been read.
+ *   slot    0 <= slot < n_adapters.  The pool's A and B name device memory the
+ *           caller owns and allows to be written.
+ * Calls that read the slot must be ordered after the copy (the same stream,
+ * or an event recorded after it): a copy on a second stream then overlaps
+ * with applies that use other slots.  Allocates nothing. */
+lora_status lora_pool_load(const lora_pool *pool, int32_t slot, const void *A_host, const void *B_host,
+                           hipStream_t stream);
 
 /* Synchronizes `stream` and stores in *count the number of invalid adapter
  * indices and segment-offset violations the last plan build met. */

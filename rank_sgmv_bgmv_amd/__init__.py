@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "lora_read_device_errors": (ctypes.c_int, [P, SZ, ctypes.POINTER(I32), P]),
             "lora_merge": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, P, I64, P]),
             "lora_merge_multi": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, I32, P, I32, P]),
+            "lora_pool_load": (ctypes.c_int, [pp, I32, P, P, P]),
             "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "lora_abi_version": (I32, []),
         }
@@ -266,6 +267,21 @@ def lora_merge_multi(shape: Pool, idx: Sequence[int], table, aligned: bool = Tru
     n = int(table.shape[0]) if table.numel() else 0
     _check(lib().lora_merge_multi(ctypes.byref(shape.c), ids, sc, len(idx), float(alpha), n, _ptr(table),
                                   1 if aligned else 0, _stream(table)), "lora_merge_multi")
+
+
+def lora_pool_load(pool: Pool, slot: int, A_host, B_host, stream=None):
+    """Copy one adapter (host tensors [r][d_in] and [d_out][r], the pool's dtype,
+    contiguous; pinned for an asynchronous copy) into slot `slot` of the pool,
+    on `stream` (a torch.cuda.Stream; the current stream by default)."""
+    torch = _torch()
+    if A_host.device.type != "cpu" or B_host.device.type != "cpu":
+        raise LoraError(-1, "A_host and B_host must be host tensors")
+    if (tuple(A_host.shape) != (pool.r, pool.d_in) or tuple(B_host.shape) != (pool.d_out, pool.r)
+            or not A_host.is_contiguous() or not B_host.is_contiguous()
+            or A_host.dtype != pool.A.dtype or B_host.dtype != pool.A.dtype):
+        raise LoraError(-2, "A_host must be [r][d_in] and B_host [d_out][r], contiguous, of the pool's dtype")
+    s = (stream or torch.cuda.current_stream(pool.A.device)).cuda_stream
+    _check(lib().lora_pool_load(ctypes.byref(pool.c), int(slot), _ptr(A_host), _ptr(B_host), s), "lora_pool_load")
 
 
 def lora_read_device_errors(plan) -> int:

@@ -389,6 +389,21 @@ lora_status lora_merge_multi(const lora_pool *shape, const int32_t *idx, const f
   return LORA_OK;
 }
 
+lora_status lora_pool_load(const lora_pool *pool, int32_t slot, const void *A_host, const void *B_host,
+                           hipStream_t stream) {
+  lora_status st = check_pool(pool);
+  if (st) return st;
+  if (!A_host || !B_host) return LORA_EINVAL;
+  if (slot < 0 || slot >= pool->n_adapters) return LORA_ESHAPE;
+  const size_t eb = size_t(elem_bytes(pool->dtype));
+  const size_t a_bytes = size_t(pool->rank) * pool->d_in * eb, b_bytes = size_t(pool->d_out) * pool->rank * eb;
+  void *A = const_cast<char *>(static_cast<const char *>(pool->A)) + size_t(slot) * a_bytes;
+  void *B = const_cast<char *>(static_cast<const char *>(pool->B)) + size_t(slot) * b_bytes;
+  if (hipMemcpyAsync(A, A_host, a_bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return LORA_EHIP;
+  if (hipMemcpyAsync(B, B_host, b_bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
 lora_status lora_read_device_errors(const void *plan, size_t plan_bytes, int32_t *count, hipStream_t stream) {
   if (!plan || !count) return LORA_EINVAL;
   if (plan_bytes < sizeof(int) * H_WORDS) return LORA_EWORKSPACE;

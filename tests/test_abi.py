@@ -155,3 +155,11 @@ def test_merge_multi_validation(lib):
     bad = (ctypes.c_int32 * 2)(0, 4)
     assert lib.lora_merge_multi(ctypes.byref(shape), bad, None, 2, 1.0, 3, FAKE, 1, None) == -1
     assert lib.lora_merge_multi(ctypes.byref(shape), ids, None, 2, 1.0, 0, FAKE, 1, None) == 0  # nothing to do
+
+
+def test_pool_load_validation(lib):
+    pool = _pool()
+    assert lib.lora_pool_load(ctypes.byref(pool), 4, FAKE, FAKE, None) == -2
+    assert lib.lora_pool_load(ctypes.byref(pool), -1, FAKE, FAKE, None) == -2
+    assert lib.lora_pool_load(ctypes.byref(pool), 0, None, FAKE, None) == -1
+    assert lib.lora_pool_load(ctypes.byref(_pool(A=None)), 0, FAKE, FAKE, None) == -1
