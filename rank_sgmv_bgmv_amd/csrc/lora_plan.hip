@@ -116,6 +116,51 @@ __device__ __forceinline__ int last_le(const int *a, int lo, int hi, int key) {
   return lo;
 }
 
+// Tile u (MFMA tiles first, then VALU tiles): its descriptor {first sorted
+// row, first request, rows, group end}, and for a VALU tile its record (rows,
+// requests, compacted slots: all rows of a tile share their adapters).
+__device__ void emit_tile(const PlanView &P, const int *__restrict__ idx, int u, int nt_m, int n_groups,
+                          const int *toff_m, const int *toff_v, const int *gstart, const int *cumlen, const int *sseg,
+                          const int *sst) {
+  const bool is_m = u < nt_m;
+  const int uu = is_m ? u : u - nt_m;
+  const int *toff = is_m ? toff_m : toff_v;
+  const int rows_per = is_m ? kMfmaRows : kValuRows;
+  const int g = last_le(toff, 0, n_groups - 1, uu);
+  const int gs = gstart[g], ge = gstart[g + 1];
+  const int p0 = cumlen[gs] + (uu - toff[g]) * rows_per;
+  const int nrows = min(rows_per, cumlen[ge] - p0);
+  const int q0 = last_le(cumlen, gs, ge - 1, p0);
+  const int4 d = make_int4(p0, q0, nrows, ge);
+  if (is_m) {
+    P.tiles_m[uu] = d;
+    return;
+  }
+  P.tiles_v[uu] = d;
+  int *R = P.vrec + (int64_t)uu * kRecWords;
+  int q = q0, nact = 0;
+  for (int w = 0; w < kValuRows * LORA_MAX_SLOTS / 4; ++w) R[R_POS + w] = 0;
+  uint8_t *pos = reinterpret_cast<uint8_t *>(R + R_POS);
+  for (int i = 0; i < nrows; ++i) {
+    const int p = p0 + i;
+    while (cumlen[q + 1] <= p) ++q;
+    const int s = sseg[q];
+    R[R_T + i] = sst[q] + (p - cumlen[q]);
+    R[R_S + i] = s;
+    int kk = 0;
+    for (int k = 0; k < P.K; ++k) {
+      const int ad = idx[(int64_t)s * P.K + k];
+      if (ad < 0 || ad >= P.n) continue;
+      if (i == 0) R[R_A + kk] = ad;
+      pos[i * LORA_MAX_SLOTS + kk] = uint8_t(k);
+      ++kk;
+    }
+    if (i == 0) nact = kk;
+  }
+  R[R_NROWS] = nrows;
+  R[R_NACT] = nact;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const int *__restrict__ seg_off,
                                                             const int *__restrict__ idx) {
   extern __shared__ int lds[];
@@ -233,47 +278,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
   __syncthreads();
 
   // 6. tile descriptors; VALU tiles also get a record
-  for (int u = tid; u < nt_m + nt_v; u += kPlanThreads) {
-    const bool is_m = u < nt_m;
-    const int uu = is_m ? u : u - nt_m;
-    const int *toff = is_m ? toff_m : toff_v;
-    const int rows_per = is_m ? kMfmaRows : kValuRows;
-    const int g = last_le(toff, 0, n_groups - 1, uu);
-    const int gs = gstart[g], ge = gstart[g + 1];
-    const int p0 = cumlen[gs] + (uu - toff[g]) * rows_per;
-    const int nrows = min(rows_per, cumlen[ge] - p0);
-    const int q0 = last_le(cumlen, gs, ge - 1, p0);
-    const int4 d = make_int4(p0, q0, nrows, ge);
-    if (is_m) {
-      P.tiles_m[uu] = d;
-    } else {
-      P.tiles_v[uu] = d;
-      // the tile's record: rows, requests, compacted slots (all rows of a tile
-      // share their adapters: one adapter, or one stacking request)
-      int *R = P.vrec + (int64_t)uu * kRecWords;
-      int q = q0, nact = 0;
-      for (int w = 0; w < kValuRows * LORA_MAX_SLOTS / 4; ++w) R[R_POS + w] = 0;
-      uint8_t *pos = reinterpret_cast<uint8_t *>(R + R_POS);
-      for (int i = 0; i < nrows; ++i) {
-        const int p = p0 + i;
-        while (cumlen[q + 1] <= p) ++q;
-        const int s = sseg[q];
-        R[R_T + i] = sst[q] + (p - cumlen[q]);
-        R[R_S + i] = s;
-        int kk = 0;
-        for (int k = 0; k < P.K; ++k) {
-          const int ad = idx[(int64_t)s * P.K + k];
-          if (ad < 0 || ad >= P.n) continue;
-          if (i == 0) R[R_A + kk] = ad;
-          pos[i * LORA_MAX_SLOTS + kk] = uint8_t(k);
-          ++kk;
-        }
-        if (i == 0) nact = kk;
-      }
-      R[R_NROWS] = nrows;
-      R[R_NACT] = nact;
-    }
-  }
+  for (int u = tid; u < nt_m + nt_v; u += kPlanThreads)
+    emit_tile(P, idx, u, nt_m, n_groups, toff_m, toff_v, gstart, cumlen, sseg, sst);
 
   // the apply kernels read these three arrays for MFMA tiles
   if (P.lds_mode) {
@@ -301,6 +307,114 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
   }
 }
 
+// Batches of at most 64 requests: one wave, one request per lane, no
+// workgroup barriers beyond the wave's own.  The counting sort becomes a rank
+// by comparison -- stable, by key and then by request, so the order inside a
+// group is fixed -- and every scan a wave scan.  Same plan as plan_kernel.
+__global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *__restrict__ seg_off,
+                                                        const int *__restrict__ idx) {
+  __shared__ int s_sseg[64], s_sst[64], s_key[64], s_cum[65], s_gstart[65], s_toff_m[65], s_toff_v[65];
+  const int lane = threadIdx.x;
+  const int S = P.S, T = P.T, n = P.n, K = P.K;
+  const bool req = lane < S;
+  int err = 0;
+  // 1. sanitised request bounds [st, en): the prefix maximum of the offsets, clamped to [0, T]
+  int st = lane, en = lane + 1;
+  if (!P.per_token) {
+    const int v0 = req ? seg_off[lane] : INT_MIN, v1 = req ? seg_off[lane + 1] : INT_MIN;
+    if (req) err += (lane == 0 && v0 < 0) + (v1 < v0) + (lane == S - 1 && v1 > T);
+    const int m = wave_incl_scan_max(v0);
+    st = min(max(m, 0), T);
+    en = min(max(max(m, v1), 0), T);
+  }
+  // 2. key: the only valid adapter, n for several (each such request is its own group), -1 for none
+  int key = -1;
+  if (req) {
+    int nact = 0, a0 = -1;
+    for (int k = 0; k < K; ++k) {
+      const int a = idx[(int64_t)lane * K + k];
+      if (a == -1) continue;
+      if (a < -1 || a >= n) { ++err; continue; }
+      if (nact == 0) a0 = a;
+      ++nact;
+    }
+    key = (en - st <= 0 || nact == 0) ? -1 : (nact == 1 ? a0 : n);
+  }
+  // 3. stable rank among the active requests
+  int rank = 0;
+  for (int j = 0; j < S; ++j) {
+    const int kj = __shfl(key, j);
+    rank += kj >= 0 && (kj < key || (kj == key && j < lane));
+  }
+  const unsigned long long act = __ballot(key >= 0);
+  const int n_active = __popcll(act);
+  if (key >= 0) {
+    s_sseg[rank] = lane;
+    s_sst[rank] = st;
+    s_key[rank] = key;
+    s_cum[rank] = en - st;
+  }
+  __syncthreads();
+  // 4. rows in sorted order and group starts
+  const bool live = lane < n_active;
+  const int len = live ? s_cum[lane] : 0, kq = live ? s_key[lane] : -1;
+  const int inc = wave_incl_scan_add(len);
+  const int total_rows = __shfl(inc, 63);
+  const int kprev = __shfl_up(kq, 1);
+  const int flag = live && (lane == 0 || kq == n || kq != kprev) ? 1 : 0;
+  const int ginc = wave_incl_scan_add(flag);
+  const int n_groups = __shfl(ginc, 63);
+  __syncthreads();
+  if (live) s_cum[lane] = inc - len;
+  if (lane == 0) s_cum[n_active] = total_rows;
+  if (flag) s_gstart[ginc - 1] = lane;
+  if (lane == 0) s_gstart[n_groups] = n_active;
+  __syncthreads();
+  // 5. tiles per group (lane g)
+  int nm = 0, nv = 0;
+  if (lane < n_groups) {
+    const int rows = s_cum[s_gstart[lane + 1]] - s_cum[s_gstart[lane]];
+    const bool big = rows >= kMfmaMinRows;
+    nm = big ? (rows + kMfmaRows - 1) / kMfmaRows : 0;
+    nv = big ? 0 : (rows + kValuRows - 1) / kValuRows;
+  }
+  const int im = wave_incl_scan_add(nm), iv = wave_incl_scan_add(nv);
+  const int nt_m = __shfl(im, 63), nt_v = __shfl(iv, 63);
+  if (lane < n_groups) {
+    s_toff_m[lane] = im - nm;
+    s_toff_v[lane] = iv - nv;
+  }
+  if (lane == 0) {
+    s_toff_m[n_groups] = nt_m;
+    s_toff_v[n_groups] = nt_v;
+  }
+  __syncthreads();
+  // 6. tile descriptors and records
+  for (int u = lane; u < nt_m + nt_v; u += 64)
+    emit_tile(P, idx, u, nt_m, n_groups, s_toff_m, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
+  // the apply kernels read these three arrays for MFMA tiles
+  if (live) {
+    P.sseg[lane] = s_sseg[lane];
+    P.sst[lane] = s_sst[lane];
+    P.cumlen[lane] = s_cum[lane];
+  }
+  if (lane == 0) P.cumlen[n_active] = total_rows;
+  for (int o = 32; o > 0; o >>= 1) err += __shfl_xor(err, o);
+  if (lane == 0) {
+    P.hdr[H_TILES_M] = nt_m;
+    P.hdr[H_TILES_V] = nt_v;
+    P.hdr[H_ERR] = err;
+    P.hdr[H_ACTIVE] = n_active;
+    P.hdr[H_GROUPS] = n_groups;
+    P.hdr[H_ROWS] = total_rows;
+    P.hdr[H_N] = n;
+    P.hdr[H_S] = S;
+    P.hdr[H_T] = T;
+    P.hdr[H_K] = K;
+    P.hdr[H_MAGIC] = kPlanMagic;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, const int *idx, hipStream_t stream) {
@@ -308,7 +422,10 @@ hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, 
       hipFuncSetAttribute(reinterpret_cast<const void *>(plan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                           int(kPlanLdsBudget)) == hipSuccess;
   (void)lds_limit_raised;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), P.lds_mode ? lds_bytes : 0, stream, P, seg_off, idx);
+  if (P.S <= 64)
+    hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(64), 0, stream, P, seg_off, idx);
+  else
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), P.lds_mode ? lds_bytes : 0, stream, P, seg_off, idx);
   return hipGetLastError();
 }
 
