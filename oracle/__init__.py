@@ -68,13 +68,13 @@ class Oracle:
         self.lib = ctypes.CDLL(path)
         self.lib.oracle_apply.restype = _I
         self.lib.oracle_apply.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P,
-                                          _P, _L, _P, _L, _P, _I, _P, _P, _P, _P, _I]
+                                          _P, _L, _P, _L, _P, _I, _P, _P, _P, _P, _I, _P]
         self.lib.oracle_shrink.restype = _I
         self.lib.oracle_shrink.argtypes = [_I, _I, _I, _I, _P, _I, _I, _P, _P, _I, _P,
-                                           _P, _L, _P, _I, _P, _P, _I]
+                                           _P, _L, _P, _I, _P, _P, _I, _P]
         self.lib.oracle_expand.restype = _I
         self.lib.oracle_expand.argtypes = [_I, _I, _I, _I, _P, _I, _I, _P, _P, _I,
-                                           _P, _L, _P, _L, _P, _I, _P, _P, _I]
+                                           _P, _L, _P, _L, _P, _I, _P, _P, _I, _P]
         self.lib.oracle_merge.restype = _I
         self.lib.oracle_merge.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _L, _I, _P, _P,
                                           ctypes.c_double, _I, _I, _P, _I]
@@ -98,7 +98,11 @@ class Oracle:
         rows = np.ascontiguousarray(rows, dtype=np.int32)
         return rows, int(rows.size)
 
-    def apply(self, dtype, A, B, x, y, *, T, S, K, seg_off, idx, scale=None, rows=None, nthreads=0):
+    @staticmethod
+    def _ranks(ranks):
+        return None if ranks is None else np.ascontiguousarray(ranks, dtype=np.int32)
+
+    def apply(self, dtype, A, B, x, y, *, T, S, K, seg_off, idx, scale=None, rows=None, nthreads=0, ranks=None):
         """Returns (y_ref [R][d_out] float64, touched [R] bool, routing [R][K] int32, macs)."""
         n, r, d_in = A.shape
         d_out = B.shape[1]
@@ -114,11 +118,12 @@ class Oracle:
         rc = self.lib.oracle_apply(DTYPE_CODE[dtype], n, r, d_in, d_out, _ptr(A), _ptr(B),
                                    T, S, _ptr(seg_off), _ptr(idx), K, _ptr(scale),
                                    _ptr(x), x.shape[1], _ptr(y), y.shape[1], _ptr(rows), R,
-                                   _ptr(y_ref), _ptr(touched), _ptr(routing), ctypes.byref(macs), nthreads)
+                                   _ptr(y_ref), _ptr(touched), _ptr(routing), ctypes.byref(macs), nthreads,
+                                   _ptr(self._ranks(ranks)))
         self._check(rc)
         return y_ref, touched.astype(bool), routing, int(macs.value)
 
-    def shrink(self, dtype, A, x, *, T, S, K, seg_off, idx, scale=None, rows=None, nthreads=0):
+    def shrink(self, dtype, A, x, *, T, S, K, seg_off, idx, scale=None, rows=None, nthreads=0, ranks=None):
         """Returns (v_ref [R][K*r] float64, touched [R] bool)."""
         n, r, d_in = A.shape
         A = np.ascontiguousarray(A); x = np.ascontiguousarray(x)
@@ -128,11 +133,11 @@ class Oracle:
         touched = np.empty(R, np.uint8)
         rc = self.lib.oracle_shrink(DTYPE_CODE[dtype], n, r, d_in, _ptr(A), T, S, _ptr(seg_off), _ptr(idx),
                                     K, _ptr(scale), _ptr(x), x.shape[1], _ptr(rows), R,
-                                    _ptr(v_ref), _ptr(touched), nthreads)
+                                    _ptr(v_ref), _ptr(touched), nthreads, _ptr(self._ranks(ranks)))
         self._check(rc)
         return v_ref, touched.astype(bool)
 
-    def expand(self, dtype, B, v, y, *, T, S, K, seg_off, idx, rows=None, nthreads=0):
+    def expand(self, dtype, B, v, y, *, T, S, K, seg_off, idx, rows=None, nthreads=0, ranks=None):
         """v: float32 [T][ldv] with v[t][k*r + j].  Returns (y_ref [R][d_out] float64, touched [R] bool)."""
         n, d_out, r = B.shape
         B = np.ascontiguousarray(B)
@@ -143,7 +148,7 @@ class Oracle:
         touched = np.empty(R, np.uint8)
         rc = self.lib.oracle_expand(DTYPE_CODE[dtype], n, r, d_out, _ptr(B), T, S, _ptr(seg_off), _ptr(idx), K,
                                     _ptr(v), v.shape[1], _ptr(y), y.shape[1], _ptr(rows), R,
-                                    _ptr(y_ref), _ptr(touched), nthreads)
+                                    _ptr(y_ref), _ptr(touched), nthreads, _ptr(self._ranks(ranks)))
         self._check(rc)
         return y_ref, touched.astype(bool)
 
@@ -164,10 +169,10 @@ class Oracle:
         return out
 
     # convenience over workloads.Case -------------------------------------
-    def apply_case(self, case, rows=None, nthreads=0):
+    def apply_case(self, case, rows=None, nthreads=0, ranks=None):
         b, p = case.batch, case.pool
         return self.apply(case.dtype, p.A, p.B, case.x, case.y, T=b.T, S=b.S, K=b.K,
-                          seg_off=b.seg_off, idx=b.idx, scale=b.scale, rows=rows, nthreads=nthreads)
+                          seg_off=b.seg_off, idx=b.idx, scale=b.scale, rows=rows, nthreads=nthreads, ranks=ranks)
 
     def shrink_case(self, case, rows=None, nthreads=0):
         b, p = case.batch, case.pool

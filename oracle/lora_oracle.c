@@ -26,6 +26,11 @@
  *   y_ref[t] = y[t]         otherwise (the row is untouched).
  *   Rows covered by no request are untouched.
  *
+ * Adapters of different ranks in one pool ("LoRA: merged or alongside": r is
+ * usually 8 to 128) are stored at the pool's rank r; with a rank array, row j
+ * of A_i and column j of B_i take part only for j < ranks[i] (what lies
+ * beyond is never read), which is the same as zero padding.
+ *
  * Readings where the pages are silent: no implicit alpha/r factor; the
  * per-slot scale defaults to 1 and multiplies the slot's contribution; an
  * index below -1 or >= n is an error here (the oracle refuses the input).
@@ -77,6 +82,14 @@ static int check_indices(int S, int K, const int32_t *idx, int n) {
     return OR_OK;
 }
 
+/* Per-adapter ranks (NULL: every adapter has rank r): each in [1, r]. */
+static int check_ranks(int n, int r, const int32_t *ranks) {
+    if (!ranks) return OR_OK;
+    for (int i = 0; i < n; ++i)
+        if (ranks[i] < 1 || ranks[i] > r) return OR_ESHAPE;
+    return OR_OK;
+}
+
 static int check_common(int n, int r, int d_in, int d_out, int T, int S, int K, int64_t ldx, int64_t ldy) {
     if (n < 0 || r < 1 || d_in < 1 || d_out < 1 || T < 0 || S < 0 || K < 1) return OR_ESHAPE;
     if (ldx < d_in || ldy < d_out) return OR_ESHAPE;
@@ -94,9 +107,11 @@ int oracle_apply(int dtype, int n, int r, int d_in, int d_out, const void *A, co
                  int T, int S, const int32_t *seg_off, const int32_t *idx, int K, const float *scale,
                  const void *x, int64_t ldx, const void *y, int64_t ldy,
                  const int32_t *rows, int n_rows,
-                 double *y_ref, uint8_t *touched, int32_t *routing, int64_t *macs, int nthreads) {
+                 double *y_ref, uint8_t *touched, int32_t *routing, int64_t *macs, int nthreads,
+                 const int32_t *ranks) {
     int rc = check_common(n, r, d_in, d_out, T, S, K, ldx, ldy);
     if (rc) return rc;
+    if ((rc = check_ranks(n, r, ranks))) return rc;
     if ((rc = check_indices(S, K, idx, n))) return rc;
     int32_t *owner = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
     if (!owner) return OR_ENOMEM;
@@ -128,7 +143,8 @@ int oracle_apply(int dtype, int n, int r, int d_in, int d_out, const void *A, co
                 if (i == -1) continue;
                 hit = 1;
                 double sc = scale ? (double)scale[(int64_t)s * K + k] : 1.0;
-                for (int j = 0; j < r; ++j) {
+                const int ri = ranks ? ranks[i] : r;  /* the adapter's own rank */
+                for (int j = 0; j < ri; ++j) {
                     double sum = 0.0;
                     for (int c = 0; c < d_in; ++c)
                         sum += elem(x, dtype, (int64_t)t * ldx + c) *
@@ -137,11 +153,11 @@ int oracle_apply(int dtype, int n, int r, int d_in, int d_out, const void *A, co
                 }
                 for (int o = 0; o < d_out; ++o) {
                     double sum = 0.0;
-                    for (int j = 0; j < r; ++j)
+                    for (int j = 0; j < ri; ++j)
                         sum += v[j] * elem(B, dtype, ((int64_t)i * d_out + o) * r + j);
                     acc[o] += sc * sum;
                 }
-                mac_total += (int64_t)r * d_in + (int64_t)d_out * r;
+                mac_total += (int64_t)ri * d_in + (int64_t)d_out * ri;
             }
             touched[q] = (uint8_t)hit;
             for (int o = 0; o < d_out; ++o) {
@@ -166,9 +182,10 @@ int oracle_apply(int dtype, int n, int r, int d_in, int d_out, const void *A, co
 int oracle_shrink(int dtype, int n, int r, int d_in, const void *A,
                   int T, int S, const int32_t *seg_off, const int32_t *idx, int K, const float *scale,
                   const void *x, int64_t ldx, const int32_t *rows, int n_rows,
-                  double *v_ref, uint8_t *touched, int nthreads) {
+                  double *v_ref, uint8_t *touched, int nthreads, const int32_t *ranks) {
     int rc = check_common(n, r, d_in, 1, T, S, K, ldx, 1);
     if (rc) return rc;
+    if ((rc = check_ranks(n, r, ranks))) return rc;
     if ((rc = check_indices(S, K, idx, n))) return rc;
     int32_t *owner = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
     if (!owner) return OR_ENOMEM;
@@ -195,12 +212,13 @@ int oracle_shrink(int dtype, int n, int r, int d_in, const void *A,
             }
             hit = 1;
             double sc = scale ? (double)scale[(int64_t)s * K + k] : 1.0;
+            const int ri = ranks ? ranks[i] : r;
             for (int j = 0; j < r; ++j) {
                 double sum = 0.0;
-                for (int c = 0; c < d_in; ++c)
+                for (int c = 0; j < ri && c < d_in; ++c)
                     sum += elem(x, dtype, (int64_t)t * ldx + c) *
                            elem(A, dtype, ((int64_t)i * r + j) * d_in + c);
-                vk[j] = sc * sum;
+                vk[j] = sc * sum;  /* 0 past the adapter's rank */
             }
         }
         touched[q] = (uint8_t)hit;
@@ -218,9 +236,11 @@ int oracle_shrink(int dtype, int n, int r, int d_in, const void *A,
 int oracle_expand(int dtype, int n, int r, int d_out, const void *B,
                   int T, int S, const int32_t *seg_off, const int32_t *idx, int K,
                   const float *v, int64_t ldv, const void *y, int64_t ldy,
-                  const int32_t *rows, int n_rows, double *y_ref, uint8_t *touched, int nthreads) {
+                  const int32_t *rows, int n_rows, double *y_ref, uint8_t *touched, int nthreads,
+                  const int32_t *ranks) {
     int rc = check_common(n, r, 1, d_out, T, S, K, 1, ldy);
     if (rc) return rc;
+    if ((rc = check_ranks(n, r, ranks))) return rc;
     if (ldv < (int64_t)K * r) return OR_ESHAPE;
     if ((rc = check_indices(S, K, idx, n))) return rc;
     int32_t *owner = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
@@ -249,8 +269,9 @@ int oracle_expand(int dtype, int n, int r, int d_out, const void *B,
             for (int k = 0; k < K; ++k) {
                 int i = idx[(int64_t)s * K + k];
                 if (i == -1) continue;
+                const int ri = ranks ? ranks[i] : r;
                 double sum = 0.0;
-                for (int j = 0; j < r; ++j)
+                for (int j = 0; j < ri; ++j)
                     sum += (double)v[(int64_t)t * ldv + (int64_t)k * r + j] *
                            elem(B, dtype, ((int64_t)i * d_out + o) * r + j);
                 acc += sum;

@@ -29,6 +29,11 @@ What pins what (pages named by title and section):
   merge_inverse    -- unmerging (alpha = -1) what was merged gives W back
                       exactly on small integers; rows subsets agree.
   merge_numpy      -- W + alpha sum_k s_k B_k A_k by numpy matmul; -1 slots skipped.
+  ranks_padding    -- "LoRA: merged or alongside" (r usually 8 to 128): adapters of
+                      different ranks in one pool; with a rank array, apply, shrink
+                      and expand equal the same calls on the pool with everything
+                      past each adapter's rank set to zero (the padding holds
+                      nonzero values here, so reading it would show).
 """
 from __future__ import annotations
 
@@ -384,9 +389,39 @@ def pin_merge_numpy(orc):
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+def pin_ranks_padding(orc):
+    rng = _rng(35)
+    n, r, d_in, d_out = 4, 8, 10, 7
+    ranks = np.array([3, 8, 1, 5], np.int32)
+    case = W.random_case(36, dtype=F32, n=n, r=r, d_in=d_in, d_out=d_out, S=6, K=2, min_len=1, max_len=4,
+                         with_scale=True)
+    p, b = case.pool, case.batch
+    A0, B0 = p.A.copy(), p.B.copy()
+    for i in range(n):
+        A0[i, ranks[i]:, :] = 0
+        B0[i, :, ranks[i]:] = 0
+    kw = dict(T=b.T, S=b.S, K=b.K, seg_off=b.seg_off, idx=b.idx, scale=b.scale)
+    y1, t1, _, m1 = orc.apply(F32, p.A, p.B, case.x, case.y, ranks=ranks, **kw)
+    y0, t0, _, m0 = orc.apply(F32, A0, B0, case.x, case.y, **kw)
+    assert np.array_equal(t1, t0) and np.allclose(y1, y0, rtol=1e-13, atol=1e-13)
+    assert m1 < m0  # fewer multiply-adds: the padding is not touched
+    v1, _ = orc.shrink(F32, p.A, case.x, ranks=ranks, **kw)
+    v0, _ = orc.shrink(F32, A0, case.x, **kw)
+    assert np.allclose(v1, v0, rtol=1e-13, atol=1e-13)
+    ekw = {k: v for k, v in kw.items() if k != "scale"}
+    vr = _f32(rng.standard_normal((b.T, b.K * r)))  # nonzero past every rank too
+    e1, _ = orc.expand(F32, p.B, vr, case.y, ranks=ranks, **ekw)
+    e0, _ = orc.expand(F32, B0, vr, case.y, **ekw)
+    assert np.allclose(e1, e0, rtol=1e-13, atol=1e-13)
+    yf, _, _, _ = orc.apply(F32, p.A, p.B, case.x, case.y, ranks=np.full(n, r, np.int32), **kw)
+    yn, _, _, _ = orc.apply(F32, p.A, p.B, case.x, case.y, **kw)
+    assert np.array_equal(yf, yn)
+
+
 ALL_PINS = [pin_merged_form, pin_rank1_closed, pin_linearity, pin_untouched, pin_permutation, pin_stacking,
             pin_numpy_special, pin_exact_bruteforce, pin_macs_formula, pin_shrink_numpy, pin_expand_numpy,
-            pin_shrink_expand_compose, pin_merge_vs_unmerged, pin_merge_rank1, pin_merge_inverse, pin_merge_numpy]
+            pin_shrink_expand_compose, pin_merge_vs_unmerged, pin_merge_rank1, pin_merge_inverse, pin_merge_numpy,
+            pin_ranks_padding]
 
 
 def run_all(orc):

@@ -23,7 +23,7 @@ MUTANTS = {
     "minus1_touches": ("if (i == -1) continue;\n                hit = 1;", "hit = 1;\n                if (i == -1) continue;", 1),
     "first_slot_only": ("for (int k = 0; k < K; ++k) {\n                int i = (s >= 0)", "for (int k = 0; k < 1; ++k) {\n                int i = (s >= 0)", 1),
     "short_d_in": ("for (int c = 0; c < d_in; ++c)", "for (int c = 0; c < d_in - 1; ++c)", 1),
-    "short_rank": ("for (int j = 0; j < r; ++j)\n                        sum += v[j]", "for (int j = 1; j < r; ++j)\n                        sum += v[j]", 1),
+    "short_rank": ("for (int j = 0; j < ri; ++j)\n                        sum += v[j]", "for (int j = 1; j < ri; ++j)\n                        sum += v[j]", 1),
     "segment_off_by_one": ("for (int t = seg_off[s]; t < seg_off[s + 1]; ++t) owner[t] = s;", "for (int t = seg_off[s] + 1; t < seg_off[s + 1]; ++t) owner[t] = s;", 1),
     "row_uses_request": ("elem(x, dtype, (int64_t)t * ldx + c) *\n                               elem(A", "elem(x, dtype, (int64_t)s * ldx + c) *\n                               elem(A", 1),
     "shrink_drops_scale": ("vk[j] = sc * sum;", "vk[j] = sum;", 1),
@@ -32,7 +32,12 @@ MUTANTS = {
                            "elem(A, dtype, ((int64_t)i * d_in + c) * r + j);\n                delta", 1),
     "merge_drops_scale": ("delta += (scale ? (double)scale[k] : 1.0) * sum;", "delta += sum;", 1),
     "merge_ignores_alpha": ("+ alpha * delta;", "+ delta;", 1),
-    "merge_uses_minus1": ("if (i == -1) continue;\n                double sum", "if (i == -1) i = 0;\n                double sum", 1),
+    "merge_uses_minus1": ("const int i = idx[k];\n                if (i == -1) continue;",
+                          "int i = idx[k];\n                if (i == -1) i = 0;", 1),
+    "ranks_ignored_in_apply": ("const int ri = ranks ? ranks[i] : r;  /* the adapter's own rank */",
+                               "const int ri = r;", 1),
+    "ranks_ignored_in_expand": ("const int ri = ranks ? ranks[i] : r;\n                double sum",
+                                "const int ri = r;\n                double sum", 1),
     "merge_first_slot_only": ("for (int k = 0; k < K; ++k) {\n                const int i = idx[k];",
                               "for (int k = 0; k < 1; ++k) {\n                const int i = idx[k];", 1),
 }
