@@ -296,6 +296,54 @@ def bench_merge_flux(dev, steps, warmup, r=64, layers=57, per_layer=4, d=3072):
             "page_model_ms_at_3350GBps": round(page_ms, 3)}
 
 
+def bench_decode_ranks(dev, steps, warmup, layers=8, n=1000, r=64, d=4096, seed=W.SEEDS["C2"]):
+    """Decode over pools stored at rank 64 whose adapters have ranks 8, 16, 32
+    or 64 (a quarter each): with the pool's rank array (only each adapter's
+    own rows and columns are read) and without it (the zero padding is read)."""
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 7)
+    ranks_np = np.random.default_rng(seed).choice([8, 16, 32, 64], size=n).astype(np.int32)
+    ranks = torch.from_numpy(ranks_np).to(dev)
+    pools = []
+    for _ in range(layers):
+        A, B = randn_pool(gen, n, r, d, d, dev)
+        mask = torch.arange(r, device=dev)[None, :] < ranks[:, None]  # [n][r]
+        A.mul_(mask[:, :, None].to(A.dtype))
+        B.mul_(mask[:, None, :].to(B.dtype))
+        pools.append((A, B))
+    xs = [randn_act(gen, 64, d, dev) for _ in range(layers)]
+    ys = [randn_act(gen, 64, d, dev) for _ in range(layers)]
+    batches = [W.batch_c2(np.random.default_rng([seed, j]), n) for j in range(16)]
+    dbs = [dev_batch(b, dev) for b in batches]
+    plan = L.new_workspace(dbs[0], n, dev)
+    table, aligned = L.problems_table([(A, B, x, y) for (A, B), x, y in zip(pools, xs, ys)], dev)
+    out = {}
+    for name, shape in (("with_ranks", L.Pool(pools[0][0], pools[0][1], ranks)),
+                        ("padded", L.Pool(pools[0][0], pools[0][1]))):
+        def step(i, ev, shape=shape):
+            db = dbs[i % 16]
+            L.lora_plan_build(db, n, plan)
+            if ev: ev[0].record()
+            L.lora_apply_multi(shape, db, plan, table, aligned)
+            if ev: ev[1].record()
+        _, k_ms, _ = Timer(steps).run(step, warmup)
+        out[name] = k_ms
+    used = [batches[i % 16] for i in range(steps)]
+    # algorithmic bytes: x, y and each distinct adapter's own rank
+    byts = []
+    for b in used:
+        ids = np.unique(b.idx[b.idx >= 0])
+        byts.append(layers * (64 * 3 * d * 2 + sum(int(ranks_np[i]) * 2 * d * 2 for i in ids)))
+    k_bytes = float(np.mean(byts))
+    return {"workload": f"decode x{layers} layers, rank-64 pools of adapters with ranks 8/16/32/64",
+            "apply_us_with_ranks": round(out["with_ranks"] * 1e3, 3), "apply_us_padded": round(out["padded"] * 1e3, 3),
+            "bytes_per_launch_own_ranks": k_bytes,
+            "GBps_with_ranks": k_bytes / (out["with_ranks"] * 1e-3) / 1e9,
+            "speedup_from_ranks": out["padded"] / out["with_ranks"]}
+
+
 def bench_pool_load(dev, reps=5, n_slots=64, r=64, d=4096, apply_reps=40):
     """Pool slot management: 64 rank-64 adapters (4096 x 4096, bf16, 1 MiB each)
     copied from page-locked host memory into pool slots with lora_pool_load on a
@@ -426,7 +474,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5,merge,poolload")
+    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5,merge,ranks,poolload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
@@ -469,6 +517,10 @@ def main():
         log("merge ...")
         torch.cuda.empty_cache()
         variants["merge_flux_r64"] = bench_merge_flux(dev, max(6, args.steps // 5), max(2, args.warmup // 5))
+    if want("ranks"):
+        log("ranks ...")
+        torch.cuda.empty_cache()
+        variants["decode_mixed_ranks"] = bench_decode_ranks(dev, args.steps, args.warmup)
     if want("poolload"):
         log("pool load ...")
         variants["pool_load_pinned"] = bench_pool_load(dev)

@@ -73,7 +73,15 @@ typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
 /* One adapted linear layer's resident, stacked adapter pool ("Serving several
  * LoRAs ...", section "Placement": every LoRA stays resident).
  *   A: [n_adapters][rank][d_in]   row-major, dtype
- *   B: [n_adapters][d_out][rank]  row-major, dtype                       */
+ *   B: [n_adapters][d_out][rank]  row-major, dtype
+ *   ranks: DEVICE [n_adapters] int32, or NULL.  Adapters of different ranks
+ *          in one pool ("LoRA: merged or alongside": r is usually 8 to 128)
+ *          are stored at `rank`; adapter i uses rows j < ranks[i] of A_i and
+ *          columns j < ranks[i] of B_i only (values are clamped to [1, rank]).
+ *          What lies past an adapter's rank is not read when its rank is a
+ *          multiple of 8 (bf16) or 4 (fp32); otherwise the rest of the last
+ *          16-byte piece is read and multiplied by zero, so it must hold finite
+ *          values.  NULL: every adapter has rank `rank`.                  */
 typedef struct {
   const void *A;
   const void *B;
@@ -82,6 +90,7 @@ typedef struct {
   int32_t d_in;
   int32_t d_out;
   lora_dtype dtype;
+  const int32_t *ranks;
 } lora_pool;
 
 /* The batch: which adapters apply to which rows.
@@ -163,7 +172,8 @@ lora_status lora_expand_planned(const lora_pool *pool, const lora_batch *batch, 
 /* Many adapted layers of one shape in ONE launch, sharing one plan: for each
  * of the n_problems entries of `problems` (a DEVICE array), the fused apply
  * with that problem's pool, x and y.  `shape` gives rank, d_in, d_out,
- * n_adapters and dtype (its A and B are ignored).  The library cannot check
+ * n_adapters, dtype and ranks (its A and B are ignored; its rank array, if
+ * any, applies to every problem).  The library cannot check
  * the pointers inside the device array; they must satisfy the alignment and
  * ld rules of lora_apply for this shape (16-byte aligned, ld a multiple of 8
  * elements for bf16 or 4 for fp32, for the vectorised path) or the launch
@@ -208,7 +218,8 @@ typedef struct {
 /* lora_merge for n_problems weights of one shape in ONE launch: for each
  * entry of `problems` (a DEVICE array), W += alpha * sum_k scale[k] B_i A_i
  * with i = idx[k] taken from that entry's pool.  `shape` gives rank, d_in,
- * d_out, n_adapters and dtype (its A and B are ignored); idx and scale are
+ * d_out, n_adapters, dtype and ranks (its A and B are ignored; its rank
+ * array, if any, applies to every problem); idx and scale are
  * HOST arrays as for lora_merge and apply to every problem.  The library
  * cannot check the pointers inside the device array: the weights must not
  * overlap one another or any pool, ldw >= d_in, and the matrix-core path

@@ -42,7 +42,7 @@ class LoraError(RuntimeError):
 class lora_pool(ctypes.Structure):
     _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("n_adapters", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
-                ("dtype", ctypes.c_int)]
+                ("dtype", ctypes.c_int), ("ranks", ctypes.c_void_p)]
 
 
 class lora_batch(ctypes.Structure):
@@ -121,17 +121,21 @@ def _check(st: int, what: str):
 
 
 class Pool:
-    """A resident adapter pool: A [n][r][d_in], B [n][d_out][r]."""
+    """A resident adapter pool: A [n][r][d_in], B [n][d_out][r]; ranks: an optional
+    int32 device tensor [n] of per-adapter ranks (adapters stored at rank r)."""
 
-    def __init__(self, A, B):
+    def __init__(self, A, B, ranks=None):
         if A.dim() != 3 or B.dim() != 3 or not A.is_contiguous() or not B.is_contiguous():
             raise LoraError(-2, "A and B must be contiguous 3-D tensors")
         n, r, d_in = A.shape
         if B.shape[0] != n or B.shape[2] != r or B.dtype != A.dtype:
             raise LoraError(-2, "B must be [n][d_out][r] with A's dtype")
-        self.A, self.B = A, B
+        if ranks is not None and (ranks.dtype != _torch().int32 or tuple(ranks.shape) != (n,)
+                                  or not ranks.is_contiguous() or ranks.device != A.device):
+            raise LoraError(-2, "ranks must be a contiguous int32 device tensor [n]")
+        self.A, self.B, self.ranks = A, B, ranks
         self.n, self.r, self.d_in, self.d_out = int(n), int(r), int(d_in), int(B.shape[1])
-        self.c = lora_pool(_ptr(A), _ptr(B), self.n, self.r, self.d_in, self.d_out, _dtype_code(A))
+        self.c = lora_pool(_ptr(A), _ptr(B), self.n, self.r, self.d_in, self.d_out, _dtype_code(A), _ptr(ranks))
 
 
 class Batch:

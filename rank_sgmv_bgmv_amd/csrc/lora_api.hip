@@ -174,6 +174,7 @@ void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Pl
   a.vrec = P.V.vrec;
   a.n = shape->n_adapters;
   a.r = shape->rank;
+  a.ranks = shape->ranks;
   a.d_in = shape->d_in;
   a.d_out = shape->d_out;
   a.kr_max = d.K * shape->rank;
@@ -239,7 +240,7 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
 
 extern "C" {
 
-int32_t lora_abi_version(void) { return 101; }
+int32_t lora_abi_version(void) { return 102; }
 
 const char *lora_status_string(lora_status s) {
   switch (s) {
@@ -342,6 +343,7 @@ lora_status merge_slots(const lora_pool *shape, const int32_t *idx, const float 
     ++a.nslots;
   }
   a.r = shape->rank;
+  a.ranks = shape->ranks;
   a.d_in = shape->d_in;
   a.d_out = shape->d_out;
   a.n_strips = (shape->d_in + 127) / 128;

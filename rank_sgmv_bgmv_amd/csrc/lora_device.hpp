@@ -180,6 +180,7 @@ constexpr int kMetaRows = kMfmaRows;  // rows of tile metadata
 struct Meta {
   int t[kMetaRows];                     // token row of each tile row
   int a[LORA_MAX_SLOTS];                // the tile's adapters (compacted slot order)
+  int rk[LORA_MAX_SLOTS];               // their ranks
   int nact;                             // valid slots
   int pad[3];
   int pos[kMetaRows][LORA_MAX_SLOTS];   // original slot index of compacted slot
@@ -198,6 +199,11 @@ __device__ __forceinline__ int rec_pos(uint2 w, int kk) {
 // Fill the metadata of a VALU tile from its record, already in registers
 // (word `tid` of it in thread tid < kRecWords); returns the tile's rows.  Only
 // per-slot scales are read from memory.  Two barriers.
+// Rank of adapter ad: its entry of the pool's rank array, clamped to [1, r].
+__device__ __forceinline__ int adapter_rank(const ApplyArgs &a, int ad) {
+  return a.ranks ? min(max(gload<int>(a.ranks + ad), 1), a.r) : a.r;
+}
+
 __device__ inline int setup_from_record(const ApplyArgs &a, int word, Meta &M) {
   const int tid = threadIdx.x;
   if (tid < kRecWords) M.rec[tid] = word;
@@ -213,7 +219,11 @@ __device__ inline int setup_from_record(const ApplyArgs &a, int word, Meta &M) {
       M.sc[tid][kk] = a.scale ? gload<float>(a.scale + (int64_t)s * a.K + k) : 1.0f;
     }
   }
-  if (tid < nact) M.a[tid] = M.rec[R_A + tid];
+  if (tid < nact) {
+    const int ad = M.rec[R_A + tid];
+    M.a[tid] = ad;
+    M.rk[tid] = adapter_rank(a, ad);
+  }
   if (tid == 0) M.nact = nact;
   __syncthreads();
   return nrows;
@@ -244,7 +254,10 @@ __device__ inline void setup_rows(const ApplyArgs &a, int4 td, int n_active, Met
       if (ad < 0 || ad >= a.n) continue;
       M.pos[tid][kk] = k;
       M.sc[tid][kk] = a.scale ? gload<float>(a.scale + (int64_t)s * a.K + k) : 1.0f;
-      if (tid == 0) M.a[kk] = ad;
+      if (tid == 0) {
+        M.a[kk] = ad;
+        M.rk[kk] = adapter_rank(a, ad);
+      }
       ++kk;
     }
     if (tid == 0) M.nact = kk;

@@ -139,6 +139,7 @@ struct ApplyArgs {
   const int *vrec;
   // shape shared by every problem
   int n, r, d_in, d_out;
+  const int *ranks;  // per-adapter ranks (device), or nullptr: every adapter has rank r
   // problems
   lora_problem single;
   const lora_problem *probs;  // device array, or nullptr => `single`
@@ -163,6 +164,7 @@ struct MergeArgs {
   float s[LORA_MAX_SLOTS];
   int nslots;  // active slots, 1 .. LORA_MAX_SLOTS
   int r, d_in, d_out;
+  const int *ranks;  // per-adapter ranks (device), or nullptr
   int n_strips;  // column strips of the matrix-core path
   int aligned;   // every problem's pointers and ldw allow 16-byte accesses
 };

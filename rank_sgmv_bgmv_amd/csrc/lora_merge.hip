@@ -79,13 +79,18 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
     uint16_t *__restrict__ W = static_cast<uint16_t *>(pr.W);
     const int64_t ldw = pr.ldw;
     auto Ak = [&](int k) { return static_cast<const uint16_t *>(pr.A) + (int64_t)a.idx[k] * r * d_in; };
+    // each slot's rank: A rows and B columns past it are not read
+    int rks[LORA_MAX_SLOTS];
+#pragma unroll
+    for (int k = 0; k < LORA_MAX_SLOTS; ++k)
+      rks[k] = (k < ns && a.ranks) ? min(max(gload<int>(a.ranks + a.idx[k]), 1), r) : r;
     auto Bk = [&](int k) { return static_cast<const uint16_t *>(pr.B) + (int64_t)a.idx[k] * d_out * r; };
     // --- stage A^T of the strip: at[k][strip_row(c)][j] = A_k[j][c0 + c], zeros past r and d_in
     for (int e = tid; e < ns * RP * (kStripCols / 8); e += kThreads) {
       const int k = e / (RP * (kStripCols / 8)), rem = e % (RP * (kStripCols / 8));
       const int j = rem / (kStripCols / 8), c = 8 * (rem % (kStripCols / 8));
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < r && c0 + c < d_in) v = gload<uint4>(Ak(k) + (int64_t)j * d_in + c0 + c);
+      if (j < rks[k] && c0 + c < d_in) v = gload<uint4>(Ak(k) + (int64_t)j * d_in + c0 + c);
       uint16_t *dst = at + ((int64_t)k * kStripCols) * AST + j;
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
         const int k = min(e / KSR, ns - 1), j = 32 * (e % KSR) + 8 * kg;
-        bv[e] = gload<uint4>(Bk(k) + (int64_t)oc * r + (j < r ? j : 0));
+        bv[e] = gload<uint4>(Bk(k) + (int64_t)oc * r + (j < rks[k] ? j : 0));
       }
     };
     auto compute = [&](int step, const uint4(&wv)[NP], const uint4(&bv)[NE]) {
@@ -128,8 +133,8 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
       for (int e = 0; e < NE; ++e) {
         const int k = e / KSR, ks = e % KSR;
         if (k < ns) {
-          // B columns past r are zero (A^T is zero there too, but B may hold anything)
-          const uint4 b = keep_if(32 * ks + 8 * kg < r, bv[e]);
+          // B columns past the slot's rank are zero (A^T is zero there too, but B may hold anything)
+          const uint4 b = keep_if(32 * ks + 8 * kg < rks[k], bv[e]);
 #pragma unroll
           for (int t = 0; t < 2 * NP; ++t) {
             const uint4 av =
@@ -206,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void merge_valu_kernel(MergeArgs a) {
       const T *__restrict__ Ak = static_cast<const T *>(pr.A) + (int64_t)a.idx[k] * r * d_in;
       const T *__restrict__ Bk = static_cast<const T *>(pr.B) + (int64_t)a.idx[k] * d_out * r;
       const float s = a.s[k];
-      for (int j = 0; j < r; ++j) {
+      const int rk = a.ranks ? min(max(gload<int>(a.ranks + a.idx[k]), 1), r) : r;
+      for (int j = 0; j < rk; ++j) {
         float av[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

@@ -84,16 +84,21 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   // ------------------------------------------------------------ shrink --
   for (int kk = 0; kk < nact; ++kk) {
     if (MODE == MODE_EXPAND) {
+      const int rk = M.rk[kk];
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
         float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int j = 16 * jt + 4 * kg;
         if (row_ok)
-          f = gload<float4>(a.v + trow * a.ldv + (int64_t)M.pos[m][kk] * R + 16 * jt + 4 * kg);
-        *vslot(kk, jt) = make_uint2(pack_bf2(f.x, f.y), pack_bf2(f.z, f.w));
+          f = gload<float4>(a.v + trow * a.ldv + (int64_t)M.pos[m][kk] * R + j);
+        // columns past the adapter's rank are zero
+        *vslot(kk, jt) = make_uint2(pack_bf2(j < rk ? f.x : 0.f, j + 1 < rk ? f.y : 0.f),
+                                    pack_bf2(j + 2 < rk ? f.z : 0.f, j + 3 < rk ? f.w : 0.f));
       }
       continue;
     }
     const uint16_t *__restrict__ Aa = static_cast<const uint16_t *>(pr.A) + (int64_t)M.a[kk] * R * d_in;
+    const int rk = M.rk[kk];  // A rows past the adapter's rank are not read (zeros in LDS)
     f32x4 acc[JT];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -105,7 +110,7 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
       for (int i = 0; i < NAV; ++i) {
         const int e = tid + i * kThreads;
         const int row = e / (KC / 8), c = kc + 8 * (e % (KC / 8));
-        ar[i] = c < d_in ? gload<uint4>(Aa + (int64_t)row * d_in + c) : make_uint4(0, 0, 0, 0);
+        ar[i] = (c < d_in && row < rk) ? gload<uint4>(Aa + (int64_t)row * d_in + c) : make_uint4(0, 0, 0, 0);
       }
     };
     auto load_x = [&](int kc, uint4(&xr)[KS]) {
@@ -133,8 +138,10 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
           for (int jt = 0; jt < JT; ++jt) {
-            const uint4 av = *reinterpret_cast<const uint4 *>(stage + (16 * jt + l16) * AST + 32 * ks + 8 * kg);
-            acc[jt] = mfma32(av, xc[ks], acc[jt]);
+            if (16 * jt < rk) {
+              const uint4 av = *reinterpret_cast<const uint4 *>(stage + (16 * jt + l16) * AST + 32 * ks + 8 * kg);
+              acc[jt] = mfma32(av, xc[ks], acc[jt]);
+            }
           }
         }
       }
@@ -173,11 +180,12 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   auto load_b = [&](int st) {
     const int ob = o_lo + (st / nact) * NO, kk = st % nact;
     const uint16_t *__restrict__ Bk = static_cast<const uint16_t *>(pr.B) + (int64_t)M.a[kk] * d_out * R;
+    const int rk = M.rk[kk];  // B columns past the adapter's rank are not read
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
       const int e = tid + i * kThreads;
       const int row = e / (R / 8), c = 8 * (e % (R / 8));
-      br[i] = ob + row < o_hi ? gload<uint4>(Bk + (int64_t)(ob + row) * R + c) : make_uint4(0, 0, 0, 0);
+      br[i] = (ob + row < o_hi && c < rk) ? gload<uint4>(Bk + (int64_t)(ob + row) * R + c) : make_uint4(0, 0, 0, 0);
     }
   };
   auto load_y = [&](int ob, uint4(&yr)[OT / 2]) {
@@ -215,14 +223,17 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
     }
     if (wave_live) {
       uint2 v[JT];
+      const int rk = M.rk[kk];
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) v[jt] = *vslot(kk, jt);
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
-          const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
-          yacc[ot] = mfma16(bv, v[jt], yacc[ot]);
+          if (16 * jt < rk) {
+            const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
+            yacc[ot] = mfma16(bv, v[jt], yacc[ot]);
+          }
         }
       }
     }

@@ -62,11 +62,12 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
 
   for (int kk = 0; kk < nact; ++kk) {
     const T *Aa = static_cast<const T *>(pr.A) + (int64_t)uniform(M.a[kk]) * r * d_in;
+    const int rk = uniform(M.rk[kk]);  // the adapter's rank: rows past it are not read, their sums are 0
     for (int j0 = w * kJPW; j0 < r; j0 += (kValuThreads / 64) * kJPW) {
       float acc[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-      for (int c0 = lane; c0 < nvx; c0 += 64 * UB) {
+      for (int c0 = lane; c0 < (j0 < rk ? nvx : 0); c0 += 64 * UB) {
         V xv[UB][MB], av[UB][kJPW];
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
@@ -75,7 +76,7 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
 #pragma unroll
           for (int m = 0; m < MB; ++m) xv[u][m] = gload_at<V>(xrow[m], off);
 #pragma unroll
-          for (int i = 0; i < kJPW; ++i) av[u][i] = gload_at<V>(Aa, uint32_t(min(j0 + i, r - 1)) * row_bytes + off);
+          for (int i = 0; i < kJPW; ++i) av[u][i] = gload_at<V>(Aa, uint32_t(min(j0 + i, rk - 1)) * row_bytes + off);
           if (cv >= nvx) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) xv[u][m] = O::zero();
@@ -98,7 +99,7 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
         const float val = wave_sum_scatter<kJPW>(part);
         const int j = j0 + lane;
         if (lane < kJPW && m < nb && j < r) {
-          const float vs = val * M.sc[m0 + m][kk];
+          const float vs = j < rk ? val * M.sc[m0 + m][kk] : 0.f;
           if constexpr (MODE == MODE_SHRINK)
             gstore(a.v + (int64_t)M.t[m0 + m] * a.ldv + (int64_t)M.pos[m0 + m][kk] * r + j, vs);
           else if constexpr (sizeof(InterT<T, VEC, MODE>) == 2)
@@ -137,7 +138,6 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
   constexpr int BS = kValuThreads * RT;  // block stride (outputs)
   const int tid = threadIdx.x;
   const int r = a.r, d_out = a.d_out, KR = a.kr_max, nact = uniform(M.nact);
-  const int nvr = r / E;
   const uint32_t brow_bytes = uint32_t(r) * sizeof(T);
   T *yrow[MB];
 #pragma unroll
@@ -164,7 +164,10 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
     for (int kk = 0; kk < nact; ++kk) {
       const T *Bk = static_cast<const T *>(pr.B) + (int64_t)uniform(M.a[kk]) * d_out * r;
       const IT *vk = s_v + kk * r;
-      for (int jv0 = 0; jv0 < nvr; jv0 += JB) {
+      // vectors of B's row past the adapter's rank are not read (the
+      // intermediate is zero there)
+      const int nvk = (uniform(M.rk[kk]) + E - 1) / E;
+      for (int jv0 = 0; jv0 < nvk; jv0 += JB) {
         V bv[NBLK][RT][JB];
 #pragma unroll
         for (int b = 0; b < NBLK; ++b)
@@ -173,12 +176,12 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj)
               bv[b][i][jj] = gload_at<V>(Bk, uint32_t(ob[b] + i) * brow_bytes +
-                                                 uint32_t(min(jv0 + jj, nvr - 1)) * (E * sizeof(T)));
+                                                 uint32_t(min(jv0 + jj, nvk - 1)) * (E * sizeof(T)));
         // vectors past the rank contribute zero (the loads above stay unconditional,
         // so they are all in flight before the first multiply)
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
-          if (jv0 + jj >= nvr) {
+          if (jv0 + jj >= nvk) {
 #pragma unroll
             for (int b = 0; b < NBLK; ++b)
 #pragma unroll
@@ -190,7 +193,7 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
           if (m < nb) {
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
-              const IT *vp = vk + m * KR + min(jv0 + jj, nvr - 1) * E;
+              const IT *vp = vk + m * KR + min(jv0 + jj, nvk - 1) * E;
               if constexpr (sizeof(IT) == 2) {
                 const V vv = *reinterpret_cast<const V *>(vp);
 #pragma unroll
@@ -265,7 +268,8 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
       // expand only: the caller's intermediate (compacted slots) into LDS
       for (int w = tid; w < nb * nact * r; w += kValuThreads) {
         const int m = w / (nact * r), rem = w % (nact * r), kk = rem / r, j = rem % r;
-        s_v[m * KR + kk * r + j] = gload<float>(a.v + (int64_t)M.t[m0 + m] * a.ldv + (int64_t)M.pos[m0 + m][kk] * r + j);
+        s_v[m * KR + kk * r + j] =
+            j < M.rk[kk] ? gload<float>(a.v + (int64_t)M.t[m0 + m] * a.ldv + (int64_t)M.pos[m0 + m][kk] * r + j) : 0.f;
       }
     }
     if (MODE == MODE_SHRINK) continue;
