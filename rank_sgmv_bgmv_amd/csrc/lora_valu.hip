@@ -219,8 +219,8 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
   }
 }
 
-// Outputs per block: rows of about 64 bytes per lane, never more than the
-// vector width, which divides d_out on the vector path (so a block never
+// Outputs per block: rows of about 64 bytes per lane (counting the rank the
+// tile uses), never more than the vector width, which divides d_out on the vector path (so a block never
 // straddles the end of a row).  Blocks per round: about 16 B vectors per lane
 // (8 with four rows).  The scalar path takes one output per thread.
 template <typename T, bool VEC, int MB, int MODE>
@@ -231,9 +231,14 @@ __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m
     valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
     return;
   } else {
-    const int row_bytes = a.r * int(sizeof(T));
+    // sized by the largest rank among the tile's slots, not the pool's stored
+    // rank: with small adapters in a pool stored at a larger rank, a lane then
+    // takes more output rows instead of repeating loads past the rank
+    int kr = 1;
+    for (int kk = 0; kk < M.nact; ++kk) kr = max(kr, M.rk[kk]);
+    const int vpr = (uniform(kr) + E - 1) / E;
+    const int row_bytes = vpr * E * int(sizeof(T));
     const int rt = min(max(64 / row_bytes, 1), E);
-    const int vpr = a.r / E;
     int nblk = expand_nvb<MB, sizeof(InterT<T, VEC, MODE>)>() / (rt * vpr);
     nblk = nblk >= 4 ? 4 : nblk >= 2 ? 2 : 1;
     while (nblk > 1 && MB * rt * nblk > 16) nblk >>= 1;  // at most 16 accumulators per lane
