@@ -69,6 +69,7 @@ typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
 #define LORA_MAX_RANK 256        /* 1 <= rank <= 256 */
 #define LORA_MAX_SLOTS 8         /* 1 <= max_slots <= 8 */
 #define LORA_MAX_SLOT_RANK 1024  /* max_slots * rank <= 1024 */
+#define LORA_MAX_SLICES 8        /* projections per group of lora_apply_sliced */
 
 /* One adapted linear layer's resident, stacked adapter pool ("Serving several
  * LoRAs ...", section "Placement": every LoRA stays resident).
@@ -181,6 +182,33 @@ lora_status lora_expand_planned(const lora_pool *pool, const lora_batch *batch, 
 lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, const void *plan, size_t plan_bytes,
                              int32_t n_problems, const lora_problem *problems, int32_t problems_aligned,
                              hipStream_t stream);
+
+/* Several projections that read the same input, in ONE launch ("Serving
+ * several LoRAs, ControlNet and IP-Adapter", answers to the self-test, the
+ * first: a LoRA attaches to attention's query, key, value and output
+ * projections, sometimes to the MLP too -- query, key and value read one
+ * input, as do an MLP's gate and up projections).
+ *
+ * `problems` (a DEVICE array of n_groups * n_slices entries) holds n_groups
+ * groups of n_slices projections each: entry g * n_slices + p is projection
+ * ("slice") p of group g, with its own pool, x and y.  Slice p's output width
+ * is d_outs[p] (a HOST array of n_slices values, the same for every group);
+ * every other size -- n_adapters, rank, d_in, dtype, ranks -- is the
+ * `shape`'s (its A, B and d_out are ignored).  1 <= n_slices <= 8.
+ *
+ * Result: for every entry, exactly what lora_apply_multi would compute for it
+ * (y += sum_k scale * (x A_i^T) B_i^T on that entry's x, pool and y).  Work is
+ * ordered tile by tile across the slices of a group, so when the slices of a
+ * group name the same x (the intended use) each row tile of x is read from
+ * HBM once for all of them and reused from cache by the others.  The y arrays
+ * of one group must not overlap each other (distinct outputs, or disjoint
+ * column ranges of one fused output with a shared ldy).  Alignment, ld rules
+ * and `problems_aligned` as for lora_apply_multi, with d_outs[p] in place of
+ * d_out; errors: LORA_ESHAPE for n_groups < 0, n_slices outside 1..8 or a
+ * d_outs value below 1, LORA_EINVAL for NULL arrays. */
+lora_status lora_apply_sliced(const lora_pool *shape, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                              int32_t n_groups, int32_t n_slices, const int32_t *d_outs,
+                              const lora_problem *problems, int32_t problems_aligned, hipStream_t stream);
 
 /* Merge stacked adapters into a weight, or unmerge them, in place ("Serving
  * several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or

@@ -9,7 +9,7 @@ the library has not been built, calls raise ``LoraError``.
 Functions carry the C names:
   lora_workspace_size, lora_plan_build, lora_apply, lora_shrink, lora_expand,
   lora_apply_planned, lora_shrink_planned, lora_expand_planned,
-  lora_apply_multi, lora_read_device_errors, lora_status_string.
+  lora_apply_multi, lora_apply_sliced, lora_read_device_errors, lora_status_string.
 
 Tensors: A [n][r][d_in] and B [n][d_out][r] contiguous (float32 or bfloat16);
 x [T][ldx], y [T][ldy] with unit column stride (ld = stride(0)); idx int32
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "lora_shrink_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
             "lora_expand_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
             "lora_apply_multi": (ctypes.c_int, [pp, pb, P, SZ, I32, P, I32, P]),
+            "lora_apply_sliced": (ctypes.c_int, [pp, pb, P, SZ, I32, I32, P, P, I32, P]),
             "lora_read_device_errors": (ctypes.c_int, [P, SZ, ctypes.POINTER(I32), P]),
             "lora_merge": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, P, I64, P]),
             "lora_merge_multi": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, I32, P, I32, P]),
@@ -235,6 +236,35 @@ def lora_apply_multi(shape: Pool, batch: Batch, plan, table, aligned: bool = Tru
     n = int(table.shape[0]) if table.numel() else 0
     _check(lib().lora_apply_multi(ctypes.byref(shape.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), n,
                                   _ptr(table), 1 if aligned else 0, _stream(plan)), "lora_apply_multi")
+
+
+def sliced_table(groups: Sequence, device):
+    """Device array of lora_problem for lora_apply_sliced.  groups: a sequence of
+    (x, [(A, B, y), ...]) -- one x and its slices (the same number of slices, of
+    the same output widths, in every group).  Returns (table, d_outs, all_aligned).
+    The tensors must stay alive while the table is used."""
+    rows, d_outs = [], None
+    for x, slices in groups:
+        widths = [int(B.shape[1]) for _, B, _ in slices]
+        if d_outs is None:
+            d_outs = widths
+        elif widths != d_outs:
+            raise LoraError(-2, "every group must have slices of the same output widths")
+        rows += [(A, B, x, y) for A, B, y in slices]
+    table, aligned = problems_table(rows, device)
+    return table, d_outs or [], aligned
+
+
+def lora_apply_sliced(shape: Pool, batch: Batch, plan, table, d_outs: Sequence[int], aligned: bool = True):
+    """Groups of projections that read one x (q / k / v, gate / up), one launch:
+    table from sliced_table; shape gives n, rank, d_in, dtype (and ranks)."""
+    ns = len(d_outs)
+    rows = int(table.shape[0]) if table.numel() else 0
+    if ns < 1 or rows % ns:
+        raise LoraError(-2, "table rows must be a whole number of groups of len(d_outs) slices")
+    widths = (ctypes.c_int32 * ns)(*[int(v) for v in d_outs])
+    _check(lib().lora_apply_sliced(ctypes.byref(shape.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), rows // ns,
+                                   ns, widths, _ptr(table), 1 if aligned else 0, _stream(plan)), "lora_apply_sliced")
 
 
 def lora_merge(pool: Pool, idx: Sequence[int], W, scale: Optional[Sequence[float]] = None, alpha: float = 1.0):

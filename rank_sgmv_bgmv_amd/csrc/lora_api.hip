@@ -114,10 +114,14 @@ struct Launch {
   size_t smem_v, smem_m;
 };
 
-Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Plan &P, int n_problems, bool vec,
-                 ApplyArgs &a) {
+// n_groups groups of ns slices; slice p writes d_outs[p] columns (plain calls:
+// one slice of the shape's d_out).
+Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Plan &P, int n_groups, int ns,
+                 const int32_t *d_outs, bool vec, ApplyArgs &a) {
   const Tune &tn = tune();
-  const int r = shape->rank, d_out = shape->d_out;
+  const int r = shape->rank;
+  int d_sum = 0;
+  for (int p = 0; p < ns; ++p) d_sum += d_outs[p];
   Launch L;
   L.vec = vec;
   const bool mfma = vec && shape->dtype == LORA_BF16 && (r == 16 || r == 32 || r == 64 || r == 128) &&
@@ -125,24 +129,34 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   L.jt = mfma ? r / 16 : 0;
   a.valu_takes_m = mfma ? 0 : 1;
 
-  // output-column chunks: more chunks per tile when there are few tiles
-  const int est_v = std::max(1, std::min(d.S, shape->n_adapters)) * n_problems;
-  const int est_m = std::max(1, (d.T + kMfmaRows - 1) / kMfmaRows) * n_problems;
+  // output-column chunks: more chunks per tile when there are few tiles; the
+  // chunk width is chosen over all slices' columns and each slice is cut
+  // into chunks of that width
+  const int est_v = std::max(1, std::min(d.S, shape->n_adapters)) * n_groups;
+  const int est_m = std::max(1, (d.T + kMfmaRows - 1) / kMfmaRows) * n_groups;
   int cv = 1, cm = 1;
   if (mode != MODE_SHRINK) {
     cv = std::min(pow2_floor(std::max(1, tn.valu_items / est_v)), tn.valu_max_chunks);
-    cv = std::max(1, std::min(cv, std::max(1, d_out / 256)));
+    cv = std::max(1, std::min(cv, std::max(1, d_sum / 256)));
     cm = pow2_floor(std::max(1, tn.mfma_items / est_m));
-    cm = std::max(1, std::min(cm, std::max(1, d_out / 512)));
+    cm = std::max(1, std::min(cm, std::max(1, d_sum / 512)));
   }
-  a.wv = round_up((d_out + cv - 1) / cv, 64);
-  a.cv = (d_out + a.wv - 1) / a.wv;
-  a.wm = round_up((d_out + cm - 1) / cm, 128);
-  a.cm = (d_out + a.wm - 1) / a.wm;
-  if (mode == MODE_SHRINK) { a.cv = a.cm = 1; a.wv = a.wm = round_up(d_out, 128); }
+  const int wv = mode == MODE_SHRINK ? round_up(d_sum, 128) : round_up((d_sum + cv - 1) / cv, 64);
+  const int wm = mode == MODE_SHRINK ? round_up(d_sum, 128) : round_up((d_sum + cm - 1) / cm, 128);
+  a.ns = ns;
+  a.cvo[0] = a.cmo[0] = 0;
+  for (int p = 0; p < ns; ++p) {
+    a.sd_out[p] = d_outs[p];
+    a.wv[p] = wv;
+    a.wm[p] = wm;
+    a.cv[p] = (d_outs[p] + wv - 1) / wv;
+    a.cm[p] = (d_outs[p] + wm - 1) / wm;
+    a.cvo[p + 1] = a.cvo[p] + a.cv[p];
+    a.cmo[p + 1] = a.cmo[p] + a.cm[p];
+  }
 
-  const int64_t items_m = (int64_t)n_problems * P.L.bound_m * a.cm;
-  const int64_t items_v = (int64_t)n_problems * ((int64_t)P.L.bound_v * a.cv + (a.valu_takes_m ? items_m : 0));
+  const int64_t items_m = (int64_t)n_groups * P.L.bound_m * a.cmo[ns];
+  const int64_t items_v = (int64_t)n_groups * ((int64_t)P.L.bound_v * a.cvo[ns]) + (a.valu_takes_m ? items_m : 0);
   L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
   L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
   L.smem_v = valu_smem_bytes(a.kr_max);
@@ -231,7 +245,7 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
   a.n_problems = 1;
   a.v = v;
   a.ldv = ldv;
-  const Launch L = configure(mode, pool, d, P, 1, vec, a);
+  const Launch L = configure(mode, pool, d, P, 1, 1, &pool->d_out, vec, a);
   if (launch_all(mode, pool->dtype, L, a, stream) != hipSuccess) return LORA_EHIP;
   return LORA_OK;
 }
@@ -240,7 +254,7 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
 
 extern "C" {
 
-int32_t lora_abi_version(void) { return 102; }
+int32_t lora_abi_version(void) { return 103; }
 
 const char *lora_status_string(lora_status s) {
   switch (s) {
@@ -323,7 +337,41 @@ lora_status lora_apply_multi(const lora_pool *shape, const lora_batch *batch, co
   fill_common(a, batch, d, P, shape);
   a.probs = problems;
   a.n_problems = n_problems;
-  const Launch L = configure(MODE_FUSED, shape, d, P, n_problems, vec, a);
+  const Launch L = configure(MODE_FUSED, shape, d, P, n_problems, 1, &shape->d_out, vec, a);
+  if (launch_all(MODE_FUSED, shape->dtype, L, a, stream) != hipSuccess) return LORA_EHIP;
+  return LORA_OK;
+}
+
+lora_status lora_apply_sliced(const lora_pool *shape, const lora_batch *batch, const void *plan, size_t plan_bytes,
+                              int32_t n_groups, int32_t n_slices, const int32_t *d_outs,
+                              const lora_problem *problems, int32_t problems_aligned, hipStream_t stream) {
+  if (!shape || !d_outs) return LORA_EINVAL;
+  if (n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_ESHAPE;
+  for (int p = 0; p < n_slices; ++p)
+    if (d_outs[p] < 1) return LORA_ESHAPE;
+  lora_pool sh = *shape;  // the shape's d_out is not used: each slice has its own
+  sh.d_out = d_outs[0];
+  shape = &sh;
+  lora_status st = check_shape(shape);
+  if (st) return st;
+  BatchDims d;
+  if ((st = check_batch(batch, d))) return st;
+  if ((int64_t)d.K * shape->rank > LORA_MAX_SLOT_RANK) return LORA_EUNSUPPORTED;
+  if (n_groups < 0) return LORA_ESHAPE;
+  if (n_groups > 0 && !problems) return LORA_EINVAL;
+  if (!aligned16(problems)) return LORA_EINVAL;
+  if ((int64_t)n_groups * n_slices > INT32_MAX) return LORA_ESHAPE;
+  Plan P;
+  if ((st = plan_for(d, shape->n_adapters, plan, plan_bytes, P))) return st;
+  if (n_groups == 0 || d.T == 0 || d.S == 0) return LORA_OK;
+  const int E = shape->dtype == LORA_BF16 ? 8 : 4;
+  bool vec = problems_aligned && shape->d_in % E == 0 && shape->rank % E == 0;
+  for (int p = 0; p < n_slices; ++p) vec = vec && d_outs[p] % E == 0;
+  ApplyArgs a;
+  fill_common(a, batch, d, P, shape);
+  a.probs = problems;
+  a.n_problems = n_groups;
+  const Launch L = configure(MODE_FUSED, shape, d, P, n_groups, n_slices, d_outs, vec, a);
   if (launch_all(MODE_FUSED, shape->dtype, L, a, stream) != hipSuccess) return LORA_EHIP;
   return LORA_OK;
 }

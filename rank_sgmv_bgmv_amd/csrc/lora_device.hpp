@@ -279,10 +279,40 @@ __device__ inline void zero_empty_slots(const ApplyArgs &a, int nrows, const Met
   }
 }
 
-// Work items are (problem, tile, output chunk).  Every XCD takes a contiguous
-// range of items (blockIdx % 8 is the XCD a workgroup is dispatched to), so all
-// chunks of a tile and the neighbouring tiles of the same adapter share that
-// XCD's L2; the workgroups of an XCD stride through its range.
+// Item q of a tile's items (in 0 .. cmo[ns] or cvo[ns]): its slice (the
+// problem of the group), that slice's output width and the chunk's columns.
+struct Chunk {
+  int slice, d_out, o_lo, o_hi;
+};
+// The slice tables are read at constant indices only (an unrolled scan): an
+// index known only at run time into the kernel's argument block makes the
+// compiler copy the array to scratch memory.
+__device__ inline Chunk chunk_of(const ApplyArgs &a, bool is_m, int q) {
+  Chunk c;
+  c.slice = 0;
+  c.d_out = a.sd_out[0];
+  int base = 0, width = is_m ? a.wm[0] : a.wv[0];
+#pragma unroll
+  for (int p = 1; p < LORA_MAX_SLICES; ++p) {
+    const int off = is_m ? a.cmo[p] : a.cvo[p];
+    if (p < a.ns && q >= off) {  // chunk offsets increase with p: the last match is q's slice
+      c.slice = p;
+      c.d_out = a.sd_out[p];
+      base = off;
+      width = is_m ? a.wm[p] : a.wv[p];
+    }
+  }
+  c.o_lo = (q - base) * width;
+  c.o_hi = min(c.d_out, c.o_lo + width);
+  return c;
+}
+
+// Work items are (group, tile, slice, output chunk), in that order: the
+// slices of a group that read one x take a tile's x in consecutive items.
+// Every XCD takes a contiguous range of items (blockIdx % 8 is the XCD a
+// workgroup is dispatched to), so all chunks of a tile and the neighbouring
+// tiles of the same adapter share that XCD's L2; the workgroups of an XCD
+// stride through its range.
 template <class F>
 __device__ inline void walk_items(int64_t n_items, F &&body) {
   if (n_items <= 0) return;

@@ -143,9 +143,17 @@ struct ApplyArgs {
   // problems
   lora_problem single;
   const lora_problem *probs;  // device array, or nullptr => `single`
-  int n_problems;
-  // output-column chunks per tile kind: cm chunks of wm columns (MFMA tiles), cv of wv (VALU tiles)
-  int cm, wm, cv, wv;
+  int n_problems;             // groups of `ns` problems (plain calls: problems)
+  // Output slices: a group of `ns` problems (entries g*ns .. g*ns+ns-1 of probs)
+  // shares the tiles; slice p writes d_out[p] columns.  A tile's work is split
+  // into output-column chunks: slice p has cv[p] chunks of wv[p] columns
+  // (VALU tiles) and cm[p] of wm[p] (MFMA tiles); cvo / cmo are their prefix
+  // sums (a tile's items across all slices: cvo[ns], cmo[ns]).  Plain calls
+  // have one slice of the shape's d_out.
+  int ns;
+  int sd_out[LORA_MAX_SLICES];
+  int cv[LORA_MAX_SLICES], wv[LORA_MAX_SLICES], cm[LORA_MAX_SLICES], wm[LORA_MAX_SLICES];
+  int cvo[LORA_MAX_SLICES + 1], cmo[LORA_MAX_SLICES + 1];
   // split API: float32 intermediate [T][ldv]
   float *v;
   int64_t ldv;

@@ -61,8 +61,8 @@ struct MfmaCfg {
 };
 
 template <int JT, int MODE>
-__device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, const Meta &M,
-                          uint16_t *stage, uint16_t *vpark) {
+__device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, int d_out,
+                          const Meta &M, uint16_t *stage, uint16_t *vpark) {
   typedef MfmaCfg<JT> C;
   constexpr int R = C::R, KC = C::KC, KS = C::KS, AST = C::AST, NAV = C::NAV;
   constexpr int NO = C::NO, OT = C::OT, BST = C::BST, NBV = C::NBV, VST = C::VST;
@@ -71,7 +71,7 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   const int m = 16 * w + l16;  // this lane's tile row
   const bool row_ok = m < nrows;
   const bool wave_live = 16 * w < nrows;
-  const int d_in = a.d_in, d_out = a.d_out, nact = M.nact;
+  const int d_in = a.d_in, nact = M.nact;
   const int64_t trow = M.t[row_ok ? m : 0];
   const uint16_t *__restrict__ xrow = static_cast<const uint16_t *>(pr.x) + trow * pr.ldx;
   uint16_t *__restrict__ yrow = static_cast<uint16_t *>(pr.y) + trow * pr.ldy;
@@ -266,16 +266,18 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
   uint16_t *vpark = reinterpret_cast<uint16_t *>(smem + kMetaBytes + MfmaCfg<JT>::LDS);
   const int n_m = gload<int>(a.hdr + H_TILES_M), n_active = gload<int>(a.hdr + H_ACTIVE);
-  const int64_t per_prob = (int64_t)n_m * a.cm;
-  walk_items(per_prob * a.n_problems, [&](int64_t item) {
-    const int p = int(item / per_prob);
-    const int64_t rem = item - (int64_t)p * per_prob;
-    const int tile = int(rem / a.cm), chunk = int(rem % a.cm);
-    const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
+  const int per_tile = a.cmo[a.ns];  // items of one tile, over every slice
+  const int64_t per_grp = (int64_t)n_m * per_tile;
+  walk_items(per_grp * a.n_problems, [&](int64_t item) {
+    const int g = int(item / per_grp);
+    const int64_t rem = item - (int64_t)g * per_grp;
+    const int tile = int(rem / per_tile);
+    const Chunk c = chunk_of(a, true, int(rem % per_tile));
+    const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + c.slice) : a.single;
     const int4 td = gload<int4>(a.tiles_m + tile);
-    const int o_lo = chunk * a.wm, o_hi = min(a.d_out, o_lo + a.wm);
     setup_rows(a, td, n_active, M);
-    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) mfma_tile<JT, MODE>(a, pr, td.z, o_lo, o_hi, M, stage, vpark);
+    if (M.nact > 0 && (MODE == MODE_SHRINK || c.o_lo < c.o_hi))
+      mfma_tile<JT, MODE>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage, vpark);
   });
 }
 

@@ -128,7 +128,7 @@ constexpr int expand_nvb() { return (IT_BYTES == 2 ? 16 : 8) / (MB >= 4 ? 2 : 1)
 // result to the y values it loaded at the start of the round.
 template <typename T, bool VEC, int MB, int RT, int NBLK, int MODE>
 __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
-                            const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi) {
+                            const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi, int d_out) {
   typedef VOps<T, VEC> O;
   typedef typename O::V V;
   typedef InterT<T, VEC, MODE> IT;
@@ -137,7 +137,7 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
   constexpr int JB = NVB / (RT * NBLK) >= 1 ? NVB / (RT * NBLK) : 1;  // vectors per output row per round
   constexpr int BS = kValuThreads * RT;  // block stride (outputs)
   const int tid = threadIdx.x;
-  const int r = a.r, d_out = a.d_out, KR = a.kr_max, nact = uniform(M.nact);
+  const int r = a.r, KR = a.kr_max, nact = uniform(M.nact);
   const uint32_t brow_bytes = uint32_t(r) * sizeof(T);
   T *yrow[MB];
 #pragma unroll
@@ -225,10 +225,10 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
 // (8 with four rows).  The scalar path takes one output per thread.
 template <typename T, bool VEC, int MB, int MODE>
 __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
-                               const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi) {
+                               const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi, int d_out) {
   constexpr int E = VOps<T, VEC>::E;
   if constexpr (!VEC) {
-    valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
     return;
   } else {
     // sized by the largest rank among the tile's slots, not the pool's stored
@@ -243,23 +243,23 @@ __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m
     nblk = nblk >= 4 ? 4 : nblk >= 2 ? 2 : 1;
     while (nblk > 1 && MB * rt * nblk > 16) nblk >>= 1;  // at most 16 accumulators per lane
     // only the (RT, NBLK) pairs within the accumulator budget are compiled
-#define LORA_EXPAND(RT_, NB_)                                                         \
-  if constexpr (MB * RT_ * NB_ <= 16) {                                               \
-    if (rt == RT_ && nblk == NB_) {                                                   \
-      valu_expand<T, VEC, MB, RT_, NB_, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);     \
-      return;                                                                         \
-    }                                                                                 \
+#define LORA_EXPAND(RT_, NB_)                                                           \
+  if constexpr (MB * RT_ * NB_ <= 16) {                                                 \
+    if (rt == RT_ && nblk == NB_) {                                                     \
+      valu_expand<T, VEC, MB, RT_, NB_, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);\
+      return;                                                                           \
+    }                                                                                   \
   }
     LORA_EXPAND(4, 4) LORA_EXPAND(4, 2) LORA_EXPAND(4, 1) LORA_EXPAND(2, 4) LORA_EXPAND(2, 2)
     LORA_EXPAND(2, 1) LORA_EXPAND(1, 4) LORA_EXPAND(1, 2)
 #undef LORA_EXPAND
-    valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    valu_expand<T, VEC, MB, 1, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
   }
 }
 
 template <typename T, bool VEC, int MODE>
-__device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, Meta &M,
-                          InterT<T, VEC, MODE> *s_v) {
+__device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, int d_out,
+                          Meta &M, InterT<T, VEC, MODE> *s_v) {
   const int tid = threadIdx.x;
   const int r = a.r, KR = a.kr_max, nact = M.nact;
   if (MODE == MODE_SHRINK) zero_empty_slots(a, nrows, M);
@@ -279,9 +279,9 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
     }
     if (MODE == MODE_SHRINK) continue;
     __syncthreads();  // the intermediate of this row block is complete
-    if (nb <= 1) valu_expand_rt<T, VEC, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-    else if (nb <= 2) valu_expand_rt<T, VEC, 2, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
-    else valu_expand_rt<T, VEC, 4, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi);
+    if (nb <= 1) valu_expand_rt<T, VEC, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
+    else if (nb <= 2) valu_expand_rt<T, VEC, 2, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
+    else valu_expand_rt<T, VEC, 4, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
     __syncthreads();  // before the next row block overwrites the intermediate
   }
 }
@@ -296,11 +296,13 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   InterT<T, VEC, MODE> *s_v = reinterpret_cast<InterT<T, VEC, MODE> *>(smem + kMetaBytes);
   const int n_m = gload<int>(a.hdr + H_TILES_M), n_v = gload<int>(a.hdr + H_TILES_V);
   const int n_active = gload<int>(a.hdr + H_ACTIVE);
-  // VALU tiles first; MFMA-sized tiles too when the MFMA kernel does not run
-  const int64_t items_v = (int64_t)n_v * a.cv;
-  const int64_t items_m = a.valu_takes_m ? (int64_t)n_m * a.cm : 0;
-  const int64_t per_prob = items_v + items_m;
-  const int64_t n_items = per_prob * a.n_problems;
+  // VALU tiles first; MFMA-sized tiles too when the MFMA kernel does not run.
+  // A tile's items run over every slice of the group (per_v / per_m of them).
+  const int per_v = a.cvo[a.ns], per_m = a.cmo[a.ns];
+  const int64_t items_v = (int64_t)n_v * per_v;
+  const int64_t items_m = a.valu_takes_m ? (int64_t)n_m * per_m : 0;
+  const int64_t per_grp = items_v + items_m;
+  const int64_t n_items = per_grp * a.n_problems;
   if (n_items <= 0) return;
   // Work items are dealt in XCD-contiguous ranges (blockIdx % 8 is the XCD):
   // the chunks of a tile and the neighbouring tiles of one problem share that
@@ -312,20 +314,26 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     const int64_t it = xcd * ipx + i;
     return it < n_items ? it : -1;
   };
-  // What an item needs before it starts -- its problem and, for a VALU tile,
-  // its record -- is loaded one item ahead, so a workgroup's next item begins
-  // without a round trip to memory.
+  // What an item needs before it starts -- where it lies, its problem and, for
+  // a VALU tile, its record -- is loaded one item ahead, so a workgroup's next
+  // item begins without a round trip to memory.
   struct Ahead {
     lora_problem pr;
-    int word;
+    int tile, q, word;  // tile, item within the tile (slice and chunk), record word
+    bool is_m;
   };
   auto load_ahead = [&](int64_t it, Ahead &h) {
-    const int p = int(it / per_prob);
-    const int64_t rem = it - (int64_t)p * per_prob;
-    h.pr = a.probs ? gload<lora_problem>(a.probs + p) : a.single;
+    const int g = int(it / per_grp);
+    int64_t rem = it - (int64_t)g * per_grp;
+    h.is_m = rem >= items_v;
+    if (h.is_m) rem -= items_v;
+    const int per = h.is_m ? per_m : per_v;
+    h.tile = int(rem / per);
+    h.q = int(rem - (int64_t)h.tile * per);
+    const int slice = chunk_of(a, h.is_m, h.q).slice;
+    h.pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + slice) : a.single;
     h.word = 0;
-    if (rem < items_v && threadIdx.x < kRecWords)
-      h.word = gload<int>(a.vrec + (rem / a.cv) * kRecWords + threadIdx.x);
+    if (!h.is_m && threadIdx.x < kRecWords) h.word = gload<int>(a.vrec + (int64_t)h.tile * kRecWords + threadIdx.x);
   };
   int64_t i = blockIdx.x >> 3;
   int64_t it = item_at(i);
@@ -337,22 +345,18 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     Ahead nxt;
     nxt.word = 0;
     if (nx >= 0) load_ahead(nx, nxt);
-    const int p = int(it / per_prob);
-    int64_t rem = it - (int64_t)p * per_prob;
-    const bool is_m = rem >= items_v;
-    if (is_m) rem -= items_v;
-    const int chunks = is_m ? a.cm : a.cv, width = is_m ? a.wm : a.wv;
-    const int tile = int(rem / chunks), chunk = int(rem % chunks);
-    const int o_lo = chunk * width, o_hi = min(a.d_out, o_lo + width);
+    const Chunk c = chunk_of(a, cur.is_m, cur.q);
+    const int o_lo = c.o_lo, o_hi = c.o_hi;
     int nrows;
-    if (is_m) {
-      const int4 td = gload<int4>(a.tiles_m + tile);
+    if (cur.is_m) {
+      const int4 td = gload<int4>(a.tiles_m + cur.tile);
       setup_rows(a, td, n_active, M);
       nrows = td.z;
     } else {
       nrows = setup_from_record(a, cur.word, M);
     }
-    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi)) valu_tile<T, VEC, MODE>(a, cur.pr, nrows, o_lo, o_hi, M, s_v);
+    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi))
+      valu_tile<T, VEC, MODE>(a, cur.pr, nrows, o_lo, o_hi, c.d_out, M, s_v);
     __syncthreads();
     it = nx;
     i += per_xcd;

@@ -40,7 +40,7 @@ def test_exported_symbols_match_binding(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lora_abi_version() == 102
+    assert lib.lora_abi_version() == 103
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.lora_status_string(st)
     assert b"workspace" in lib.lora_status_string(-3)
@@ -115,6 +115,20 @@ def test_split_and_multi_validation(lib):
     assert lib.lora_apply_multi(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, None, 1, None) == -1
     assert lib.lora_apply_multi(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, 16, 2, FAKE, 1, None) == -3
     assert lib.lora_apply_multi(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, -1, FAKE, 1, None) == -2
+    # sliced: host array of output widths, 1..8 slices, each width >= 1
+    w3 = (ctypes.c_int32 * 3)(64, 16, 16)
+    sl = lib.lora_apply_sliced
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, 3, None, FAKE, 1, None) == -1
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, 3, w3, None, 1, None) == -1
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, 0, w3, FAKE, 1, None) == -2
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, 9, w3, FAKE, 1, None) == -2
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, -1, 3, w3, FAKE, 1, None) == -2
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, 3, (ctypes.c_int32 * 3)(64, 0, 16),
+              FAKE, 1, None) == -2
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, 16, 2, 3, w3, FAKE, 1, None) == -3
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 2, 3, w3, FAKE + 4, 1, None) == -1
+    # zero groups: nothing to do (no launch)
+    assert sl(ctypes.byref(pool), ctypes.byref(batch), FAKE * 2000, ws_bytes, 0, 3, w3, None, 1, None) == 0
     assert lib.lora_plan_build(ctypes.byref(batch), 0, FAKE * 2000, ws_bytes, None) == -2
     assert lib.lora_plan_build(ctypes.byref(batch), 4, FAKE * 2000, 16, None) == -3
     cnt = ctypes.c_int32(0)
