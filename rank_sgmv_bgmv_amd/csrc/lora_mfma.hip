@@ -138,10 +138,10 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
           for (int jt = 0; jt < JT; ++jt) {
-            if (16 * jt < rk) {
-              const uint4 av = *reinterpret_cast<const uint4 *>(stage + (16 * jt + l16) * AST + 32 * ks + 8 * kg);
-              acc[jt] = mfma32(av, xc[ks], acc[jt]);
-            }
+            // rows past the adapter's rank are zeros in the stage (no branch
+            // here: a condition per rank tile would split the MFMA chain)
+            const uint4 av = *reinterpret_cast<const uint4 *>(stage + (16 * jt + l16) * AST + 32 * ks + 8 * kg);
+            acc[jt] = mfma32(av, xc[ks], acc[jt]);
           }
         }
       }
@@ -223,17 +223,16 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
     }
     if (wave_live) {
       uint2 v[JT];
-      const int rk = M.rk[kk];
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) v[jt] = *vslot(kk, jt);
+      // B columns past the adapter's rank are zeros in the stage and so is the
+      // intermediate there: those products add exact zeros
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
-          if (16 * jt < rk) {
-            const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
-            yacc[ot] = mfma16(bv, v[jt], yacc[ot]);
-          }
+          const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
+          yacc[ot] = mfma16(bv, v[jt], yacc[ot]);
         }
       }
     }
