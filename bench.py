@@ -49,7 +49,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # those sources change.
 TRAFFIC_SOURCES = ["rank_sgmv_bgmv_amd/csrc/lora_valu.hip", "rank_sgmv_bgmv_amd/csrc/lora_device.hpp",
                    "rank_sgmv_bgmv_amd/csrc/lora_internal.hpp"]
-MEASURED_TRAFFIC = {"sources_sha256_16": "04d94b94d412b5ff", "fetch_kib": 181261.0, "write_kib": 16384.0,
+MEASURED_TRAFFIC = {"sources_sha256_16": "6ea0dd008d8abab2", "fetch_kib": 179740.3, "write_kib": 16384.0,
                     "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -254,6 +254,78 @@ def bench_c4_stack(dev, steps, warmup, seed=W.SEEDS["C4"]):
         flops += len(probs) * accounting.lora_flops(slot_tokens, r, d_in, d_out)
     return result("llama3-8b stack 32x7 mixed", wall, steps, touched, byts, flops, k_ms, byts, flops, len(launches),
                   {"distinct_adapters": distinct, "note": "apply_* covers the 4 multi-problem launches together"})
+
+
+def bench_c4_shared_x(dev, steps, warmup, seed=W.SEEDS["C4"], modes=("multi", "sliced")):
+    """The Llama-3-8B-shaped stack with the model's own input sharing: per layer,
+    query / key / value read one x and gate / up read another.  Timed two ways
+    on the same data: one multi-problem launch per projection shape (q,o | k,v |
+    gate,up | down: a shared x is fetched once per projection) and the sliced
+    launches (q/k/v | o | gate/up | down: a tile of x is fetched once per group).
+    Bytes: the minimum, with each shared x read once."""
+    torch = torch_mod()
+    import rank_sgmv_bgmv_amd as L
+    r, n, layers = 32, 256, W.LLAMA3_8B_LAYERS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 1)
+    batch = W.batch_c4(np.random.default_rng(seed), n)
+    db = dev_batch(batch, dev)
+    T = batch.T
+    dims = {name: (d_in, d_out) for name, d_in, d_out in W.LLAMA3_8B_PROJ}
+    per_layer = []
+    for _ in range(layers):
+        x_attn, x_o, x_mlp, x_down = (randn_act(gen, T, dims[k][0], dev) for k in ("q", "o", "gate", "down"))
+        proj = {}
+        for name, (d_in, d_out) in dims.items():
+            A, B = randn_pool(gen, n, r, d_in, d_out, dev)
+            proj[name] = (A, B, randn_act(gen, T, d_out, dev))
+        per_layer.append(({"q": x_attn, "k": x_attn, "v": x_attn, "o": x_o, "gate": x_mlp, "up": x_mlp,
+                           "down": x_down}, proj))
+    shape_groups = [("q", "o"), ("k", "v"), ("gate", "up"), ("down",)]
+    multi = []
+    for names in shape_groups:
+        probs = [(proj[k][0], proj[k][1], xs[k], proj[k][2]) for xs, proj in per_layer for k in names]
+        table, aligned = L.problems_table(probs, dev)
+        multi.append((L.Pool(probs[0][0], probs[0][1]), table, aligned))
+    slice_groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    sliced = []
+    for names in slice_groups:
+        groups = [(xs[names[0]], [proj[k] for k in names]) for xs, proj in per_layer]
+        table, d_outs, aligned = L.sliced_table(groups, dev)
+        sliced.append((L.Pool(groups[0][1][0][0], groups[0][1][0][1]), table, d_outs, aligned))
+    plan = L.new_workspace(db, n, dev)
+    torch.cuda.synchronize()
+
+    def step_multi(i, ev):
+        L.lora_plan_build(db, n, plan)
+        if ev: ev[0].record()
+        for shape, table, aligned in multi:
+            L.lora_apply_multi(shape, db, plan, table, aligned)
+        if ev: ev[1].record()
+
+    def step_sliced(i, ev):
+        L.lora_plan_build(db, n, plan)
+        if ev: ev[0].record()
+        for shape, table, d_outs, aligned in sliced:
+            L.lora_apply_sliced(shape, db, plan, table, d_outs, aligned)
+        if ev: ev[1].record()
+
+    ms_multi = ms_sliced = wall = float("nan")
+    if "multi" in modes:
+        wall, ms_multi, _ = Timer(steps).run(step_multi, warmup)
+    if "sliced" in modes:
+        wall, ms_sliced, _ = Timer(steps).run(step_sliced, warmup)
+    touched, slot_tokens, distinct = accounting.batch_work(batch.seg_bounds(), batch.idx, n)
+    byts = layers * sum(accounting.sliced_call_bytes(touched, distinct, r, dims[names[0]][0],
+                                                     [dims[k][1] for k in names], 2) for names in slice_groups)
+    flops = layers * sum(accounting.lora_flops(slot_tokens, r, d_in, d_out) for d_in, d_out in dims.values())
+    k_ms = ms_sliced if "sliced" in modes else ms_multi
+    res = result("llama3-8b stack 32x7 mixed, shared x", wall, steps, touched, byts, flops, k_ms, byts, flops,
+                 len(sliced), {"distinct_adapters": distinct})
+    res.update({"apply_us_per_shape_multi": round(ms_multi * 1e3, 3), "apply_us_sliced": round(ms_sliced * 1e3, 3),
+                "speedup_sliced": ms_multi / ms_sliced,
+                "note": "apply_* covers the 4 sliced launches; bytes count each shared x once"})
+    return res
 
 
 def bench_merge_flux(dev, steps, warmup, r=64, layers=57, per_layer=4, d=3072):
@@ -474,7 +546,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c5,merge,ranks,poolload")
+    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c4x,c5,merge,ranks,poolload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
@@ -517,6 +589,12 @@ def main():
         log("merge ...")
         torch.cuda.empty_cache()
         variants["merge_flux_r64"] = bench_merge_flux(dev, max(6, args.steps // 5), max(2, args.warmup // 5))
+    if want("c4x"):
+        log("c4 shared x ...")
+        torch.cuda.empty_cache()
+        modes = tuple(m for m in ("multi", "sliced") if os.environ.get("LORA_BENCH_C4X_MODE", m) == m)
+        variants["C4_llama3_8b_shared_x"] = bench_c4_shared_x(dev, max(3, args.steps // 4), max(1, args.warmup // 2),
+                                                              modes=modes)
     if want("ranks"):
         log("ranks ...")
         torch.cuda.empty_cache()

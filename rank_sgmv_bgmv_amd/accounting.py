@@ -30,6 +30,14 @@ def call_bytes(touched_tokens: int, distinct_adapters: int, r: int, d_in: int, d
     return touched_tokens * (d_in + 2 * d_out) * elem + distinct_adapters * adapter_bytes(r, d_in, d_out, elem)
 
 
+def sliced_call_bytes(touched_tokens: int, distinct_adapters: int, r: int, d_in: int, d_outs, elem: int) -> int:
+    """Algorithmic HBM bytes of one group of projections that read one x: x read
+    once for the group, each projection's y read and written once, each used
+    adapter of each projection read once."""
+    return (touched_tokens * (d_in + 2 * sum(d_outs)) * elem
+            + distinct_adapters * sum(adapter_bytes(r, d_in, d, elem) for d in d_outs))
+
+
 def batch_work(seg_bounds: Iterable, idx, n_adapters: int):
     """(touched tokens, slot-tokens, distinct adapters) of a batch.
     seg_bounds: [(start, end)] per request; idx: [S][K] with -1 = empty."""
