@@ -17,6 +17,7 @@ struct Tune {
   int valu_max_chunks = 8;
   int mfma_items = 256;   // aim for about this many MFMA work items per launch
   int grid_cap = 2048;    // workgroups per launch; the kernels grid-stride over items
+  int mfma_half = -1;     // MFMA half-size stages: -1 when they let two workgroups share a CU, 0 never, 1 always
 };
 
 int env_int(const char *name, int dflt) {
@@ -32,6 +33,7 @@ const Tune &tune() {
     x.valu_max_chunks = env_int("LORA_VALU_MAX_CHUNKS", x.valu_max_chunks);
     x.mfma_items = env_int("LORA_MFMA_ITEMS", x.mfma_items);
     x.grid_cap = env_int("LORA_GRID_CAP", x.grid_cap);
+    x.mfma_half = env_int("LORA_MFMA_HALF", x.mfma_half);
     return x;
   }();
   return t;
@@ -110,6 +112,7 @@ int pow2_floor(int x) {
 struct Launch {
   bool vec;
   int jt;           // rank / 16 when the MFMA kernel runs, else 0
+  bool half;        // MFMA kernel with half-size stages
   int grid_v, grid_m;
   size_t smem_v, smem_m;
 };
@@ -160,14 +163,24 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
   L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
   L.smem_v = valu_smem_bytes(a.kr_max);
-  L.smem_m = mfma ? mfma_smem_bytes(L.jt, d.K) : 0;
+  // Two MFMA workgroups per CU when they fit in LDS: with many stacked slots
+  // (each parks a 64-row intermediate) the half-size stages make them fit.
+  L.half = false;
+  L.smem_m = mfma ? mfma_smem_bytes(L.jt, d.K, false) : 0;
+  const bool want_half = tn.mfma_half < 0 ? (L.smem_m > kMaxLdsBytes / 2 &&
+                                              mfma_smem_bytes(L.jt, d.K, true) <= kMaxLdsBytes / 2)
+                                           : tn.mfma_half > 0;
+  if (mfma && want_half && mfma_half_available(L.jt)) {
+    L.half = true;
+    L.smem_m = mfma_smem_bytes(L.jt, d.K, true);
+  }
   return L;
 }
 
 // MFMA tiles (the long groups) first, then the VALU tiles.
 hipError_t launch_all(int mode, int dtype, const Launch &L, const ApplyArgs &a, hipStream_t stream) {
   if (L.jt > 0) {
-    hipError_t e = launch_mfma(mode, L.jt, a, L.grid_m, L.smem_m, stream);
+    hipError_t e = launch_mfma(mode, L.jt, L.half, a, L.grid_m, L.smem_m, stream);
     if (e != hipSuccess) return e;
   }
   return launch_valu(mode, dtype, L.vec, a, L.grid_v, L.smem_v, stream);

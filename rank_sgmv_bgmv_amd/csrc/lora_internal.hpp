@@ -180,7 +180,9 @@ bool merge_mfma_eligible(const MergeArgs &a, int dtype);
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t stream);
 
 size_t valu_smem_bytes(int kr_max);
-size_t mfma_smem_bytes(int jt, int slots);
+// MFMA kernel LDS per workgroup; `half`: the half-size stages (ranks 64 / 128 only).
+size_t mfma_smem_bytes(int jt, int slots, bool half);
+bool mfma_half_available(int jt);
 
 hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, const int *idx, hipStream_t stream);
 
@@ -188,6 +190,7 @@ hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, 
 hipError_t launch_valu(int mode, int dtype, bool vec, const ApplyArgs &args, int grid, size_t smem,
                        hipStream_t stream);
 // MFMA kernel (bf16, vector path): jt = rank / 16 in {1, 2, 4, 8}.
-hipError_t launch_mfma(int mode, int jt, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
+hipError_t launch_mfma(int mode, int jt, bool half, const ApplyArgs &args, int grid, size_t smem,
+                       hipStream_t stream);
 
 }  // namespace lora

@@ -44,26 +44,29 @@ __device__ __forceinline__ f32x4 mfma16(uint2 a, uint2 b, f32x4 c) {
                                                     0, 0);
 }
 
-template <int JT>
+// HS = 2 halves both stages (d_in columns per shrink stage, outputs per expand
+// stage): less LDS per workgroup, for tiles with many stacked slots, whose
+// parked intermediates would otherwise leave room for one workgroup per CU.
+template <int JT, int HS = 1>
 struct MfmaCfg {
   static constexpr int R = 16 * JT;
-  static constexpr int KC = R <= 64 ? 256 : 128;           // d_in columns per shrink stage
+  static constexpr int KC = (R <= 64 ? 256 : 128) / HS;    // d_in columns per shrink stage
   static constexpr int KS = KC / 32;                       // k-steps per stage
   static constexpr int AST = KC + 8;                       // staged A row stride (elements)
   static constexpr int NAV = R * (KC / 8) / kThreads;      // 16-byte A pieces per thread per stage
-  static constexpr int NO = 128;                           // outputs per expand stage
+  static constexpr int NO = 128 / HS;                      // outputs per expand stage
   static constexpr int OT = NO / 16;                       // 16-wide output tiles per stage
   static constexpr int BST = R + 8;                        // staged B row stride (elements)
   static constexpr int NBV = NO * (R / 8) / kThreads;      // 16-byte B pieces per thread per stage
   static constexpr size_t LDS = (size_t(R) * AST > size_t(NO) * BST ? size_t(R) * AST : size_t(NO) * BST) * 2;
   static constexpr int VST = R + 8;                        // row stride (elements) of the parked intermediate
-  static_assert(NAV >= 1 && NBV >= 1, "stage sizes");
+  static_assert(NAV >= 1 && NBV >= 1 && KC % 32 == 0 && NO % 32 == 0, "stage sizes");
 };
 
-template <int JT, int MODE>
+template <int JT, int HS, int MODE>
 __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, int d_out,
                           const Meta &M, uint16_t *stage, uint16_t *vpark) {
-  typedef MfmaCfg<JT> C;
+  typedef MfmaCfg<JT, HS> C;
   constexpr int R = C::R, KC = C::KC, KS = C::KS, AST = C::AST, NAV = C::NAV;
   constexpr int NO = C::NO, OT = C::OT, BST = C::BST, NBV = C::NBV, VST = C::VST;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -258,12 +261,12 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
 }
 
 // ---------------------------------------------------------------- kernel --
-template <int JT, int MODE>
+template <int JT, int HS, int MODE>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Meta &M = *reinterpret_cast<Meta *>(smem);
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
-  uint16_t *vpark = reinterpret_cast<uint16_t *>(smem + kMetaBytes + MfmaCfg<JT>::LDS);
+  uint16_t *vpark = reinterpret_cast<uint16_t *>(smem + kMetaBytes + MfmaCfg<JT, HS>::LDS);
   const int n_m = gload<int>(a.hdr + H_TILES_M), n_active = gload<int>(a.hdr + H_ACTIVE);
   const int per_tile = a.cmo[a.ns];  // items of one tile, over every slice
   const int64_t per_grp = (int64_t)n_m * per_tile;
@@ -276,28 +279,28 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
     const int4 td = gload<int4>(a.tiles_m + tile);
     setup_rows(a, td, n_active, M);
     if (M.nact > 0 && (MODE == MODE_SHRINK || c.o_lo < c.o_hi))
-      mfma_tile<JT, MODE>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage, vpark);
+      mfma_tile<JT, HS, MODE>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage, vpark);
   });
 }
 
 // Launch one instantiation; the first launch lifts its dynamic-LDS limit to
 // the 160 KB a gfx950 workgroup may use.
-template <int JT, int M>
+template <int JT, int HS, int M>
 hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_kernel<JT, M>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_kernel<JT, HS, M>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
-  hipLaunchKernelGGL((mfma_kernel<JT, M>), dim3(grid), dim3(kThreads), smem, stream, a);
+  hipLaunchKernelGGL((mfma_kernel<JT, HS, M>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
-template <int JT>
+template <int JT, int HS>
 hipError_t launch_jt(int mode, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   switch (mode) {
-    case MODE_FUSED: return launch_one<JT, MODE_FUSED>(a, grid, smem, stream);
-    case MODE_SHRINK: return launch_one<JT, MODE_SHRINK>(a, grid, smem, stream);
-    case MODE_EXPAND: return launch_one<JT, MODE_EXPAND>(a, grid, smem, stream);
+    case MODE_FUSED: return launch_one<JT, HS, MODE_FUSED>(a, grid, smem, stream);
+    case MODE_SHRINK: return launch_one<JT, HS, MODE_SHRINK>(a, grid, smem, stream);
+    case MODE_EXPAND: return launch_one<JT, HS, MODE_EXPAND>(a, grid, smem, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -305,22 +308,30 @@ hipError_t launch_jt(int mode, const ApplyArgs &a, int grid, size_t smem, hipStr
 }  // namespace
 
 // Meta + staging + the parked intermediate of up to `slots` slots.
-size_t mfma_smem_bytes(int jt, int slots) {
+template <int JT, int HS>
+size_t smem_of(int slots) {
+  return kMetaBytes + MfmaCfg<JT, HS>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<JT, HS>::VST * 2;
+}
+
+size_t mfma_smem_bytes(int jt, int slots, bool half) {
   switch (jt) {
-    case 1: return kMetaBytes + MfmaCfg<1>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<1>::VST * 2;
-    case 2: return kMetaBytes + MfmaCfg<2>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<2>::VST * 2;
-    case 4: return kMetaBytes + MfmaCfg<4>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<4>::VST * 2;
-    case 8: return kMetaBytes + MfmaCfg<8>::LDS + size_t(slots) * kMfmaRows * MfmaCfg<8>::VST * 2;
+    case 1: return smem_of<1, 1>(slots);
+    case 2: return smem_of<2, 1>(slots);
+    case 4: return half ? smem_of<4, 2>(slots) : smem_of<4, 1>(slots);
+    case 8: return half ? smem_of<8, 2>(slots) : smem_of<8, 1>(slots);
   }
   return 0;
 }
 
-hipError_t launch_mfma(int mode, int jt, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+// Half stages are built for ranks 64 and 128 only: smaller ranks park little.
+bool mfma_half_available(int jt) { return jt == 4 || jt == 8; }
+
+hipError_t launch_mfma(int mode, int jt, bool half, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   switch (jt) {
-    case 1: return launch_jt<1>(mode, a, grid, smem, stream);
-    case 2: return launch_jt<2>(mode, a, grid, smem, stream);
-    case 4: return launch_jt<4>(mode, a, grid, smem, stream);
-    case 8: return launch_jt<8>(mode, a, grid, smem, stream);
+    case 1: return launch_jt<1, 1>(mode, a, grid, smem, stream);
+    case 2: return launch_jt<2, 1>(mode, a, grid, smem, stream);
+    case 4: return half ? launch_jt<4, 2>(mode, a, grid, smem, stream) : launch_jt<4, 1>(mode, a, grid, smem, stream);
+    case 8: return half ? launch_jt<8, 2>(mode, a, grid, smem, stream) : launch_jt<8, 1>(mode, a, grid, smem, stream);
   }
   return hipErrorInvalidValue;
 }

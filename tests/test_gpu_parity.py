@@ -46,6 +46,13 @@ GRID = {
     "bf16_k2_r64_chunks": dict(dtype=W.BF16, n=4, r=64, d_in=256, d_out=1024, S=6, K=2, min_len=0, max_len=100),
     "bf16_k4_r128_mfma": dict(dtype=W.BF16, n=6, r=128, d_in=128, d_out=128, S=4, K=4, min_len=20, max_len=90,
                               with_scale=True, p_empty=0.2),
+    # three stacked rank-128 slots / six rank-64 slots: the MFMA kernel takes
+    # its half-size stages (two workgroups per CU fit in LDS only then); d_in
+    # and d_out end inside a stage
+    "bf16_k3_r128_half_stages": dict(dtype=W.BF16, n=6, r=128, d_in=200, d_out=200, S=5, K=3, min_len=20,
+                                     max_len=150, with_scale=True, p_empty=0.2),
+    "bf16_k6_r64_half_stages": dict(dtype=W.BF16, n=8, r=64, d_in=320, d_out=192, S=4, K=6, min_len=30,
+                                    max_len=120, p_empty=0.1),
     "bf16_k5_r128_valu": dict(dtype=W.BF16, n=6, r=128, d_in=64, d_out=64, S=3, K=5, min_len=10, max_len=40,
                               p_empty=0.2),
     "bf16_r256": dict(dtype=W.BF16, n=3, r=256, d_in=128, d_out=96, S=5, min_len=1, max_len=30),
