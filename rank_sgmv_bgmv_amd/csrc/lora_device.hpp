@@ -229,12 +229,50 @@ __device__ inline int setup_from_record(const ApplyArgs &a, int word, Meta &M) {
   return nrows;
 }
 
+// Compacted slots of request s for tile rows 0 .. nrows-1 that all belong to
+// it: `ad` / `sc` hold the request's K adapter indices and scales (thread
+// order, already in LDS).
+__device__ inline void compact_slots(const ApplyArgs &a, const int *ad, const float *sc, int row, Meta &M) {
+  int kk = 0;
+  for (int k = 0; k < a.K; ++k) {
+    const int i = ad[k];
+    if (i < 0 || i >= a.n) continue;
+    M.pos[row][kk] = k;
+    M.sc[row][kk] = sc[k];
+    if (row == 0) {
+      M.a[kk] = i;
+      M.rk[kk] = adapter_rank(a, i);
+    }
+    ++kk;
+  }
+  if (row == 0) M.nact = kk;
+}
+
 // Fill an MFMA-sized tile's rows (token index, compacted slots, scales) into
-// LDS: the rows' requests are found by a binary search over the sorted rows'
-// prefix sums, staged in LDS with one parallel load.  Ends with a barrier.
+// LDS.  A tile inside one request (td.w >= 0: td.y is the request, td.w its
+// first token row) needs one round of loads, its slots and scales.  A tile
+// that spans requests finds each row's request by a binary search over the
+// sorted rows' prefix sums, staged in LDS with one parallel load, then loads
+// every slot of the row at once.  Ends with a barrier.
 __device__ inline void setup_rows(const ApplyArgs &a, int4 td, int n_active, Meta &M) {
   const int tid = threadIdx.x;
   const int p0 = td.x, q0 = td.y, nrows = td.z;
+  if (td.w >= 0) {
+    int *ad = M.rec;
+    float *sc = reinterpret_cast<float *>(M.rec + LORA_MAX_SLOTS);
+    if (tid < LORA_MAX_SLOTS) {
+      const int64_t e = (int64_t)q0 * a.K + min(tid, a.K - 1);
+      ad[tid] = gload<int>(a.idx + e);
+      sc[tid] = a.scale ? gload<float>(a.scale + e) : 1.0f;
+    }
+    __syncthreads();
+    if (tid < nrows) {
+      M.t[tid] = td.w + tid;
+      compact_slots(a, ad, sc, tid, M);
+    }
+    __syncthreads();
+    return;
+  }
   // a tile's rows lie in requests q0 .. q0 + nrows - 1 (each holds >= 1 row)
   const int nq = min(nrows, n_active - q0);
   if (tid <= nq) M.cum[tid] = gload<int>(a.cumlen + q0 + tid);

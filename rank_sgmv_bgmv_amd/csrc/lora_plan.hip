@@ -133,7 +133,12 @@ __device__ void emit_tile(const PlanView &P, const int *__restrict__ idx, int u,
   const int q0 = last_le(cumlen, gs, ge - 1, p0);
   const int4 d = make_int4(p0, q0, nrows, ge);
   if (is_m) {
-    P.tiles_m[uu] = d;
+    // A tile inside one request carries that request and its first token row
+    // ({p0, request, rows, first token row}); one that spans requests carries
+    // {p0, first sorted request, rows, -1} and its rows are found through the
+    // prefix sums.
+    const bool single = cumlen[q0 + 1] >= p0 + nrows;
+    P.tiles_m[uu] = single ? make_int4(p0, sseg[q0], nrows, sst[q0] + (p0 - cumlen[q0])) : make_int4(p0, q0, nrows, -1);
     return;
   }
   P.tiles_v[uu] = d;
