@@ -319,6 +319,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
 __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *__restrict__ seg_off,
                                                         const int *__restrict__ idx) {
   __shared__ int s_sseg[64], s_sst[64], s_key[64], s_cum[65], s_gstart[65], s_toff_m[65], s_toff_v[65];
+  __shared__ int s_idx[64 * LORA_MAX_SLOTS];  // the batch's idx [S][K], read once from memory
+  __shared__ __align__(16) int s_keyin[64];    // every request's key, for the rank
   const int lane = threadIdx.x;
   const int S = P.S, T = P.T, n = P.n, K = P.K;
   const bool req = lane < S;
@@ -333,23 +335,45 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
     en = min(max(max(m, v1), 0), T);
   }
   // 2. key: the only valid adapter, n for several (each such request is its own group), -1 for none
+  // (every slot's index in flight at once, clamped addresses; kept in LDS for
+  // the tile records)
+  int ads[LORA_MAX_SLOTS];
+#pragma unroll
+  for (int k = 0; k < LORA_MAX_SLOTS; ++k) ads[k] = req ? idx[(int64_t)lane * K + min(k, K - 1)] : -1;
   int key = -1;
   if (req) {
     int nact = 0, a0 = -1;
-    for (int k = 0; k < K; ++k) {
-      const int a = idx[(int64_t)lane * K + k];
-      if (a == -1) continue;
-      if (a < -1 || a >= n) { ++err; continue; }
-      if (nact == 0) a0 = a;
-      ++nact;
+#pragma unroll
+    for (int k = 0; k < LORA_MAX_SLOTS; ++k) {
+      if (k < K) {
+        const int a = ads[k];
+        s_idx[lane * K + k] = a;
+        if (a != -1) {
+          if (a < -1 || a >= n) {
+            ++err;
+          } else {
+            if (nact == 0) a0 = a;
+            ++nact;
+          }
+        }
+      }
     }
     key = (en - st <= 0 || nact == 0) ? -1 : (nact == 1 ? a0 : n);
   }
-  // 3. stable rank among the active requests
+  // 3. stable rank among the active requests: every key is read back from LDS
+  // in 16-byte pieces, all in flight at once (a cross-lane read per key would
+  // wait for each in turn)
+  s_keyin[lane] = key;
+  __syncthreads();
   int rank = 0;
-  for (int j = 0; j < S; ++j) {
-    const int kj = __shfl(key, j);
-    rank += kj >= 0 && (kj < key || (kj == key && j < lane));
+#pragma unroll
+  for (int j4 = 0; j4 < 16; ++j4) {
+    const int4 q = reinterpret_cast<const int4 *>(s_keyin)[j4];
+    const int j = 4 * j4;
+    rank += q.x >= 0 && (q.x < key || (q.x == key && j < lane));
+    rank += q.y >= 0 && (q.y < key || (q.y == key && j + 1 < lane));
+    rank += q.z >= 0 && (q.z < key || (q.z == key && j + 2 < lane));
+    rank += q.w >= 0 && (q.w < key || (q.w == key && j + 3 < lane));
   }
   const unsigned long long act = __ballot(key >= 0);
   const int n_active = __popcll(act);
@@ -396,7 +420,7 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   __syncthreads();
   // 6. tile descriptors and records
   for (int u = lane; u < nt_m + nt_v; u += 64)
-    emit_tile(P, idx, u, nt_m, n_groups, s_toff_m, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
+    emit_tile(P, s_idx, u, nt_m, n_groups, s_toff_m, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
   // the apply kernels read these three arrays for MFMA tiles
   if (live) {
     P.sseg[lane] = s_sseg[lane];
