@@ -21,7 +21,10 @@
 //     the expand's v_mfma_f32_16x16x16_bf16.  Each lane parks them in LDS
 //     (its own row, read back only by itself) until the expand.
 //   Expand: Y^T[o][t] += sum_j B[o][j] v[t][j] per stage of 128 outputs (and
-//     per slot).  B is staged through LDS with the next stage prefetched into
+//     per slot).  (A second build halves both stages -- d_in columns per
+//     shrink stage, outputs per expand stage -- for tiles with many stacked
+//     slots, whose parked intermediates would otherwise leave LDS for one
+//     workgroup per CU.)  B is staged through LDS with the next stage prefetched into
 //     registers; y is read one stage ahead straight into the accumulator
 //     layout, added and rounded once to bf16, and written back.  The B rows
 //     of each pair of 16-wide output tiles are interleaved as they are staged
