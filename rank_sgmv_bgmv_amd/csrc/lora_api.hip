@@ -102,6 +102,18 @@ lora_status plan_for(const BatchDims &d, int n, const void *ws, size_t ws_bytes,
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Compute units of the current device (looked up once per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
 int pow2_floor(int x) {
   int p = 1;
   while (p * 2 <= x) p *= 2;
@@ -158,7 +170,7 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     a.cmo[p + 1] = a.cmo[p] + a.cm[p];
   }
 
-  const int64_t items_m = (int64_t)n_groups * P.L.bound_m * a.cmo[ns];
+  const int64_t items_m = (int64_t)n_groups * std::max(P.L.bound_m, P.L.bound_ms) * a.cmo[ns];
   const int64_t items_v = (int64_t)n_groups * ((int64_t)P.L.bound_v * a.cvo[ns]) + (a.valu_takes_m ? items_m : 0);
   L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
   L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
@@ -174,6 +186,10 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     L.half = true;
     L.smem_m = mfma_smem_bytes(L.jt, d.K, true);
   }
+  // what the MFMA kernel needs to choose between the plan's two tilings
+  a.n_cu = cu_count();
+  const int per_cu = L.smem_m ? (int)std::min<size_t>(2, std::max<size_t>(1, kMaxLdsBytes / L.smem_m)) : 2;
+  a.mfma_slots = a.n_cu * per_cu;
   return L;
 }
 
@@ -197,6 +213,7 @@ void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Pl
   a.sst = P.V.sst;
   a.cumlen = P.V.cumlen;
   a.tiles_m = P.V.tiles_m;
+  a.tiles_ms = P.V.tiles_ms;
   a.tiles_v = P.V.tiles_v;
   a.vrec = P.V.vrec;
   a.n = shape->n_adapters;

@@ -14,6 +14,7 @@ constexpr int kPlanThreads = 1024;  // one workgroup builds the plan
 constexpr int kThreads = 256;       // apply kernels: 4 wave64s per workgroup
 constexpr int kValuThreads = 256;   // VALU kernel workgroup
 constexpr int kMfmaRows = 64;       // rows per MFMA tile (16 per wave)
+constexpr int kMfmaRowsSmall = 48;  // rows per MFMA tile of the plan's second tiling (the fourth wave idles)
 constexpr int kValuRows = 4;        // rows per VALU tile (one row block: heavy adapters become several tiles)
 constexpr int kMfmaMinRows = 17;    // adapter groups with at least this many rows get MFMA tiles
 constexpr int kRowBlock = 4;        // rows per VALU pass (register budget of the VALU tile body)
@@ -47,14 +48,16 @@ enum {
   H_ROWS = 5,      // rows covered by active requests
   H_N = 6, H_S = 7, H_T = 8, H_K = 9,
   H_MAGIC = 10,
+  H_TILES_MS = 11,  // number of MFMA tiles of the second (kMfmaRowsSmall-row) tiling
   H_WORDS = 64
 };
 constexpr int kPlanMagic = 0x4c6f5241;  // "LoRA"
 
 // Byte offsets of the plan arrays inside the workspace.
 struct PlanLayout {
-  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, tiles_m, tiles_v, vrec, total;
-  int S, T, n, bound_m, bound_v;
+  size_t hdr, start, key, cnt, cur, sseg, sst, cumlen, gtmp, gstart, toff_m, toff_v, toff_ms, tiles_m, tiles_v,
+      tiles_ms, vrec, total;
+  int S, T, n, bound_m, bound_v, bound_ms;
   size_t lds_bytes;  // LDS the plan kernel uses for its working arrays (0: they stay in global memory)
 };
 
@@ -68,6 +71,7 @@ inline PlanLayout plan_layout(int S, int T, int n) {
   L.S = S; L.T = T; L.n = n;
   L.bound_m = (T + kMfmaRows - 1) / kMfmaRows + S + 1;
   L.bound_v = (T + kValuRows - 1) / kValuRows + S + 1;
+  L.bound_ms = (T + kMfmaRowsSmall - 1) / kMfmaRowsSmall + S + 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.hdr = take(sizeof(int) * H_WORDS);
@@ -82,21 +86,23 @@ inline PlanLayout plan_layout(int S, int T, int n) {
   L.gstart = take(sizeof(int) * (size_t(S) + 2));
   L.toff_m = take(sizeof(int) * (size_t(S) + 2));
   L.toff_v = take(sizeof(int) * (size_t(S) + 2));
+  L.toff_ms = take(sizeof(int) * (size_t(S) + 2));
   L.tiles_m = take(sizeof(int4) * size_t(L.bound_m));
   L.tiles_v = take(sizeof(int4) * size_t(L.bound_v));
+  L.tiles_ms = take(sizeof(int4) * size_t(L.bound_ms));
   L.vrec = take(sizeof(int) * kRecWords * size_t(L.bound_v));
   L.total = off;
-  // working arrays: start, key, sseg, sst (S+1 each), cumlen, gtmp, gstart, toff_m, toff_v (S+2 each),
-  // cnt, cur (n+2 each)
-  const size_t lds_ints = 4 * (size_t(S) + 1) + 5 * (size_t(S) + 2) + 2 * (size_t(n) + 2);
+  // working arrays: start, key, sseg, sst (S+1 each), cumlen, gtmp, gstart, toff_m, toff_v, toff_ms (S+2
+  // each), cnt, cur (n+2 each)
+  const size_t lds_ints = 4 * (size_t(S) + 1) + 6 * (size_t(S) + 2) + 2 * (size_t(n) + 2);
   L.lds_bytes = lds_ints * sizeof(int) <= kPlanLdsBudget ? lds_ints * sizeof(int) : 0;
   return L;
 }
 
 // Device view of a plan.
 struct PlanView {
-  int *hdr, *start, *key, *cnt, *cur, *sseg, *sst, *cumlen, *gtmp, *gstart, *toff_m, *toff_v;
-  int4 *tiles_m, *tiles_v;
+  int *hdr, *start, *key, *cnt, *cur, *sseg, *sst, *cumlen, *gtmp, *gstart, *toff_m, *toff_v, *toff_ms;
+  int4 *tiles_m, *tiles_v, *tiles_ms;
   int *vrec;  // per VALU tile: a record of kRecWords words
   int S, T, n, K, per_token;
   int lds_mode;
@@ -117,8 +123,10 @@ inline PlanView plan_view(void *ws, const PlanLayout &L, int K, int per_token) {
   P.gstart = reinterpret_cast<int *>(b + L.gstart);
   P.toff_m = reinterpret_cast<int *>(b + L.toff_m);
   P.toff_v = reinterpret_cast<int *>(b + L.toff_v);
+  P.toff_ms = reinterpret_cast<int *>(b + L.toff_ms);
   P.tiles_m = reinterpret_cast<int4 *>(b + L.tiles_m);
   P.tiles_v = reinterpret_cast<int4 *>(b + L.tiles_v);
+  P.tiles_ms = reinterpret_cast<int4 *>(b + L.tiles_ms);
   P.vrec = reinterpret_cast<int *>(b + L.vrec);
   P.S = L.S; P.T = L.T; P.n = L.n; P.K = K; P.per_token = per_token;
   P.lds_mode = L.lds_bytes > 0;
@@ -136,6 +144,7 @@ struct ApplyArgs {
   // plan (read only)
   const int *hdr, *sseg, *sst, *cumlen;
   const int4 *tiles_m, *tiles_v;
+  const int4 *tiles_ms;  // the plan's second MFMA tiling (kMfmaRowsSmall rows per tile)
   const int *vrec;
   // shape shared by every problem
   int n, r, d_in, d_out;
@@ -160,6 +169,8 @@ struct ApplyArgs {
   // layout of dynamic LDS
   int kr_max;      // max_slots * rank (row stride of the VALU intermediate)
   int valu_takes_m;  // the VALU kernel also runs the MFMA-sized tiles (no MFMA kernel launched)
+  // MFMA tiling choice: the CUs of the device and the MFMA workgroups that fit on it at once
+  int n_cu, mfma_slots;
 };
 
 // Merge / unmerge of stacked adapters into weights: for every problem p,

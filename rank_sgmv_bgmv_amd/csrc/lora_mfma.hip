@@ -270,8 +270,18 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
   Meta &M = *reinterpret_cast<Meta *>(smem);
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
   uint16_t *vpark = reinterpret_cast<uint16_t *>(smem + kMetaBytes + MfmaCfg<JT, HS>::LDS);
-  const int n_m = gload<int>(a.hdr + H_TILES_M), n_active = gload<int>(a.hdr + H_ACTIVE);
+  const int n_m64 = gload<int>(a.hdr + H_TILES_M), n_ms = gload<int>(a.hdr + H_TILES_MS);
+  const int n_active = gload<int>(a.hdr + H_ACTIVE);
   const int per_tile = a.cmo[a.ns];  // items of one tile, over every slice
+  // The plan's 48-row tiling when the 64-row items are more than the CUs (so
+  // some CUs would run two and set the launch's duration) but the 48-row items
+  // all fit on the chip at once: the CUs that run two then hold 96 rows
+  // instead of 128.  With more items than that, 64-row tiles (their adapter
+  // staging spread over more rows) are faster.
+  const bool small = (int64_t)n_m64 * per_tile * a.n_problems > a.n_cu &&
+                     (int64_t)n_ms * per_tile * a.n_problems <= a.mfma_slots;
+  const int n_m = small ? n_ms : n_m64;
+  const int4 *tiles = small ? a.tiles_ms : a.tiles_m;
   const int64_t per_grp = (int64_t)n_m * per_tile;
   walk_items(per_grp * a.n_problems, [&](int64_t item) {
     const int g = int(item / per_grp);
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
     const int tile = int(rem / per_tile);
     const Chunk c = chunk_of(a, true, int(rem % per_tile));
     const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + c.slice) : a.single;
-    const int4 td = gload<int4>(a.tiles_m + tile);
+    const int4 td = gload<int4>(tiles + tile);
     setup_rows(a, td, n_active, M);
     if (M.nact > 0 && (MODE == MODE_SHRINK || c.o_lo < c.o_hi))
       mfma_tile<JT, HS, MODE>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage, vpark);

@@ -119,28 +119,36 @@ __device__ __forceinline__ int last_le(const int *a, int lo, int hi, int key) {
 // Tile u (MFMA tiles first, then VALU tiles): its descriptor {first sorted
 // row, first request, rows, group end}, and for a VALU tile its record (rows,
 // requests, compacted slots: all rows of a tile share their adapters).
-__device__ void emit_tile(const PlanView &P, const int *__restrict__ idx, int u, int nt_m, int n_groups,
-                          const int *toff_m, const int *toff_v, const int *gstart, const int *cumlen, const int *sseg,
-                          const int *sst) {
-  const bool is_m = u < nt_m;
-  const int uu = is_m ? u : u - nt_m;
-  const int *toff = is_m ? toff_m : toff_v;
-  const int rows_per = is_m ? kMfmaRows : kValuRows;
+// Descriptor of tile uu of an MFMA tiling of `rows_per` rows per tile (toff:
+// the tiling's first tile of each group).  A tile inside one request carries
+// that request and its first token row ({p0, request, rows, first token row});
+// one that spans requests carries {p0, first sorted request, rows, -1} and its
+// rows are found through the prefix sums.
+__device__ int4 mfma_tile_desc(const int *toff, int rows_per, int uu, int n_groups, const int *gstart,
+                               const int *cumlen, const int *sseg, const int *sst) {
   const int g = last_le(toff, 0, n_groups - 1, uu);
   const int gs = gstart[g], ge = gstart[g + 1];
   const int p0 = cumlen[gs] + (uu - toff[g]) * rows_per;
   const int nrows = min(rows_per, cumlen[ge] - p0);
   const int q0 = last_le(cumlen, gs, ge - 1, p0);
-  const int4 d = make_int4(p0, q0, nrows, ge);
-  if (is_m) {
-    // A tile inside one request carries that request and its first token row
-    // ({p0, request, rows, first token row}); one that spans requests carries
-    // {p0, first sorted request, rows, -1} and its rows are found through the
-    // prefix sums.
-    const bool single = cumlen[q0 + 1] >= p0 + nrows;
-    P.tiles_m[uu] = single ? make_int4(p0, sseg[q0], nrows, sst[q0] + (p0 - cumlen[q0])) : make_int4(p0, q0, nrows, -1);
+  const bool single = cumlen[q0 + 1] >= p0 + nrows;
+  return single ? make_int4(p0, sseg[q0], nrows, sst[q0] + (p0 - cumlen[q0])) : make_int4(p0, q0, nrows, -1);
+}
+
+__device__ void emit_tile(const PlanView &P, const int *__restrict__ idx, int u, int nt_m, int n_groups,
+                          const int *toff_m, const int *toff_v, const int *gstart, const int *cumlen, const int *sseg,
+                          const int *sst) {
+  if (u < nt_m) {
+    P.tiles_m[u] = mfma_tile_desc(toff_m, kMfmaRows, u, n_groups, gstart, cumlen, sseg, sst);
     return;
   }
+  const int uu = u - nt_m;
+  const int g = last_le(toff_v, 0, n_groups - 1, uu);
+  const int gs = gstart[g], ge = gstart[g + 1];
+  const int p0 = cumlen[gs] + (uu - toff_v[g]) * kValuRows;
+  const int nrows = min(kValuRows, cumlen[ge] - p0);
+  const int q0 = last_le(cumlen, gs, ge - 1, p0);
+  const int4 d = make_int4(p0, q0, nrows, ge);
   P.tiles_v[uu] = d;
   int *R = P.vrec + (int64_t)uu * kRecWords;
   int q = q0, nact = 0;
@@ -177,7 +185,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
   // Working arrays: in LDS when they fit (small batches: no global round trips
   // between the phases), else in the workspace.  Flat pointers serve both.
   int *start = P.start, *key = P.key, *cnt = P.cnt, *cur = P.cur, *sseg = P.sseg, *sst = P.sst,
-      *cumlen = P.cumlen, *gtmp = P.gtmp, *gstart = P.gstart, *toff_m = P.toff_m, *toff_v = P.toff_v;
+      *cumlen = P.cumlen, *gtmp = P.gtmp, *gstart = P.gstart, *toff_m = P.toff_m, *toff_v = P.toff_v,
+      *toff_ms = P.toff_ms;
   if (P.lds_mode) {
     int *q = lds;
     start = q; q += S + 1;
@@ -189,6 +198,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
     gstart = q; q += S + 2;
     toff_m = q; q += S + 2;
     toff_v = q; q += S + 2;
+    toff_ms = q; q += S + 2;
     cnt = q; q += n + 2;
     cur = q;
   }
@@ -275,16 +285,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
     const bool big = rows >= kMfmaMinRows;
     toff_m[g] = big ? (rows + kMfmaRows - 1) / kMfmaRows : 0;
     toff_v[g] = big ? 0 : (rows + kValuRows - 1) / kValuRows;
+    toff_ms[g] = big ? (rows + kMfmaRowsSmall - 1) / kMfmaRowsSmall : 0;
   }
   __syncthreads();
   const int nt_m = chunked_excl_scan(toff_m, toff_m, n_groups, sh);
   const int nt_v = chunked_excl_scan(toff_v, toff_v, n_groups, sh);
-  if (tid == 0) { toff_m[n_groups] = nt_m; toff_v[n_groups] = nt_v; }
+  const int nt_ms = chunked_excl_scan(toff_ms, toff_ms, n_groups, sh);
+  if (tid == 0) { toff_m[n_groups] = nt_m; toff_v[n_groups] = nt_v; toff_ms[n_groups] = nt_ms; }
   __syncthreads();
 
-  // 6. tile descriptors; VALU tiles also get a record
+  // 6. tile descriptors; VALU tiles also get a record; then the second MFMA tiling
   for (int u = tid; u < nt_m + nt_v; u += kPlanThreads)
     emit_tile(P, idx, u, nt_m, n_groups, toff_m, toff_v, gstart, cumlen, sseg, sst);
+  for (int u = tid; u < nt_ms; u += kPlanThreads)
+    P.tiles_ms[u] = mfma_tile_desc(toff_ms, kMfmaRowsSmall, u, n_groups, gstart, cumlen, sseg, sst);
 
   // the apply kernels read these three arrays for MFMA tiles
   if (P.lds_mode) {
@@ -298,6 +312,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
 
   __syncthreads();
   if (tid == 0) {
+    P.hdr[H_TILES_MS] = nt_ms;
     P.hdr[H_TILES_M] = nt_m;
     P.hdr[H_TILES_V] = nt_v;
     P.hdr[H_ERR] = s_err;
@@ -318,7 +333,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
 // group is fixed -- and every scan a wave scan.  Same plan as plan_kernel.
 __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *__restrict__ seg_off,
                                                         const int *__restrict__ idx) {
-  __shared__ int s_sseg[64], s_sst[64], s_key[64], s_cum[65], s_gstart[65], s_toff_m[65], s_toff_v[65];
+  __shared__ int s_sseg[64], s_sst[64], s_key[64], s_cum[65], s_gstart[65], s_toff_m[65], s_toff_v[65], s_toff_ms[65];
   __shared__ int s_idx[64 * LORA_MAX_SLOTS];  // the batch's idx [S][K], read once from memory
   __shared__ __align__(16) int s_keyin[64];    // every request's key, for the rank
   const int lane = threadIdx.x;
@@ -400,27 +415,32 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   if (lane == 0) s_gstart[n_groups] = n_active;
   __syncthreads();
   // 5. tiles per group (lane g)
-  int nm = 0, nv = 0;
+  int nm = 0, nv = 0, nms = 0;
   if (lane < n_groups) {
     const int rows = s_cum[s_gstart[lane + 1]] - s_cum[s_gstart[lane]];
     const bool big = rows >= kMfmaMinRows;
     nm = big ? (rows + kMfmaRows - 1) / kMfmaRows : 0;
     nv = big ? 0 : (rows + kValuRows - 1) / kValuRows;
+    nms = big ? (rows + kMfmaRowsSmall - 1) / kMfmaRowsSmall : 0;
   }
-  const int im = wave_incl_scan_add(nm), iv = wave_incl_scan_add(nv);
-  const int nt_m = __shfl(im, 63), nt_v = __shfl(iv, 63);
+  const int im = wave_incl_scan_add(nm), iv = wave_incl_scan_add(nv), ims = wave_incl_scan_add(nms);
+  const int nt_m = __shfl(im, 63), nt_v = __shfl(iv, 63), nt_ms = __shfl(ims, 63);
   if (lane < n_groups) {
     s_toff_m[lane] = im - nm;
     s_toff_v[lane] = iv - nv;
+    s_toff_ms[lane] = ims - nms;
   }
   if (lane == 0) {
     s_toff_m[n_groups] = nt_m;
     s_toff_v[n_groups] = nt_v;
+    s_toff_ms[n_groups] = nt_ms;
   }
   __syncthreads();
   // 6. tile descriptors and records
   for (int u = lane; u < nt_m + nt_v; u += 64)
     emit_tile(P, s_idx, u, nt_m, n_groups, s_toff_m, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
+  for (int u = lane; u < nt_ms; u += 64)
+    P.tiles_ms[u] = mfma_tile_desc(s_toff_ms, kMfmaRowsSmall, u, n_groups, s_gstart, s_cum, s_sseg, s_sst);
   // the apply kernels read these three arrays for MFMA tiles
   if (live) {
     P.sseg[lane] = s_sseg[lane];
@@ -430,6 +450,7 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   if (lane == 0) P.cumlen[n_active] = total_rows;
   for (int o = 32; o > 0; o >>= 1) err += __shfl_xor(err, o);
   if (lane == 0) {
+    P.hdr[H_TILES_MS] = nt_ms;
     P.hdr[H_TILES_M] = nt_m;
     P.hdr[H_TILES_V] = nt_v;
     P.hdr[H_ERR] = err;
