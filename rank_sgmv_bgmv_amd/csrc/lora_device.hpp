@@ -347,18 +347,16 @@ __device__ inline Chunk chunk_of(const ApplyArgs &a, bool is_m, int q) {
 
 // Work items are (group, tile, slice, output chunk), in that order: the
 // slices of a group that read one x take a tile's x in consecutive items.
-// Every XCD takes a contiguous range of items (blockIdx % 8 is the XCD a
-// workgroup is dispatched to), so all chunks of a tile and the neighbouring
-// tiles of the same adapter share that XCD's L2; the workgroups of an XCD
-// stride through its range.
+// Items are dealt round-robin over the workgroups, and so over the XCDs
+// (blockIdx % 8 is the XCD a workgroup is dispatched to): tiles of very
+// different cost (a request with three stacked adapters runs three shrink
+// and expand passes) sit next to each other in the plan's order, and
+// contiguous ranges per XCD left a few XCDs with all the long tiles.  The
+// adapter a group's tiles share is then staged from each XCD's L2 (or the
+// shared cache behind them) rather than one.
 template <class F>
 __device__ inline void walk_items(int64_t n_items, F &&body) {
-  if (n_items <= 0) return;
-  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-  const int64_t ipx = (n_items + 7) >> 3;
-  for (int64_t i = lb; i < ipx; i += per_xcd) {
-    const int64_t item = xcd * ipx + i;
-    if (item >= n_items) break;
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     body(item);
     __syncthreads();
   }
