@@ -286,7 +286,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
   walk_items(per_grp * a.n_problems, [&](int64_t item) {
     const int g = int(item / per_grp);
     const int64_t rem = item - (int64_t)g * per_grp;
-    const int tile = int(rem / per_tile);
+    // tiles in reverse plan order: the plan puts the requests with several
+    // adapters (the longest tiles: a shrink and an expand pass per slot)
+    // last, and they should start first rather than form the launch's tail
+    const int tile = n_m - 1 - int(rem / per_tile);
     const Chunk c = chunk_of(a, true, int(rem % per_tile));
     const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + c.slice) : a.single;
     const int4 td = gload<int4>(tiles + tile);
