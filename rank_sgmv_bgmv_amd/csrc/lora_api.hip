@@ -171,7 +171,9 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   }
 
   const int64_t items_m = (int64_t)n_groups * std::max(P.L.bound_m, P.L.bound_ms) * a.cmo[ns];
-  const int64_t items_v = (int64_t)n_groups * ((int64_t)P.L.bound_v * a.cvo[ns]) + (a.valu_takes_m ? items_m : 0);
+  // the VALU kernel takes an MFMA-sized tile as one item per row block
+  const int64_t items_mv = (int64_t)n_groups * P.L.bound_m * a.cmo[ns] * (kMfmaRows / kRowBlock);
+  const int64_t items_v = (int64_t)n_groups * ((int64_t)P.L.bound_v * a.cvo[ns]) + (a.valu_takes_m ? items_mv : 0);
   L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
   L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
   L.smem_v = valu_smem_bytes(a.kr_max);

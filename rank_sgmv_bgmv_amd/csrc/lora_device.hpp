@@ -305,9 +305,9 @@ __device__ inline void setup_rows(const ApplyArgs &a, int4 td, int n_active, Met
 
 // Zero the intermediate columns of the empty slots of every row of a tile
 // (lora_shrink writes every column of a touched row).
-__device__ inline void zero_empty_slots(const ApplyArgs &a, int nrows, const Meta &M) {
-  for (int e = threadIdx.x; e < nrows * a.K; e += blockDim.x) {
-    const int m = e / a.K, k = e % a.K;
+__device__ inline void zero_empty_slots(const ApplyArgs &a, int row_lo, int row_hi, const Meta &M) {
+  for (int e = threadIdx.x; e < (row_hi - row_lo) * a.K; e += blockDim.x) {
+    const int m = row_lo + e / a.K, k = e % a.K;
     bool used = false;
     for (int kk = 0; kk < M.nact; ++kk) used |= (M.pos[m][kk] == k);
     if (!used) {

@@ -172,7 +172,7 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
     }
   }
   if (MODE == MODE_SHRINK) {
-    zero_empty_slots(a, nrows, M);
+    zero_empty_slots(a, 0, nrows, M);
     return;
   }
 

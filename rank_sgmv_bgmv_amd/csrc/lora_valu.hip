@@ -257,14 +257,15 @@ __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m
   }
 }
 
+// Rows row_lo .. row_hi-1 of a tile, in blocks of kRowBlock rows.
 template <typename T, bool VEC, int MODE>
-__device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi, int d_out,
-                          Meta &M, InterT<T, VEC, MODE> *s_v) {
+__device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int row_lo, int row_hi, int o_lo, int o_hi,
+                          int d_out, Meta &M, InterT<T, VEC, MODE> *s_v) {
   const int tid = threadIdx.x;
   const int r = a.r, KR = a.kr_max, nact = M.nact;
-  if (MODE == MODE_SHRINK) zero_empty_slots(a, nrows, M);
-  for (int m0 = 0; m0 < nrows; m0 += kRowBlock) {
-    const int nb = min(kRowBlock, nrows - m0);
+  if (MODE == MODE_SHRINK) zero_empty_slots(a, row_lo, row_hi, M);
+  for (int m0 = row_lo; m0 < row_hi; m0 += kRowBlock) {
+    const int nb = min(kRowBlock, row_hi - m0);
     if (MODE != MODE_EXPAND) {
       if (nb <= 1) valu_shrink<T, VEC, 1, MODE>(a, pr, m0, nb, M, s_v);
       else if (nb <= 2) valu_shrink<T, VEC, 2, MODE>(a, pr, m0, nb, M, s_v);
@@ -296,9 +297,12 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   InterT<T, VEC, MODE> *s_v = reinterpret_cast<InterT<T, VEC, MODE> *>(smem + kMetaBytes);
   const int n_m = gload<int>(a.hdr + H_TILES_M), n_v = gload<int>(a.hdr + H_TILES_V);
   const int n_active = gload<int>(a.hdr + H_ACTIVE);
-  // VALU tiles first; MFMA-sized tiles too when the MFMA kernel does not run.
-  // A tile's items run over every slice of the group (per_v / per_m of them).
-  const int per_v = a.cvo[a.ns], per_m = a.cmo[a.ns];
+  // VALU tiles first; MFMA-sized tiles too when the MFMA kernel does not run,
+  // each as kSubBlocks items of kRowBlock rows (one workgroup would otherwise
+  // take a 64-row tile's row blocks one after another).  A tile's items run
+  // over every slice of the group (per_v / per_m of them per row block).
+  constexpr int kSubBlocks = kMfmaRows / kRowBlock;
+  const int per_v = a.cvo[a.ns], per_m = a.cmo[a.ns] * kSubBlocks;
   const int64_t items_v = (int64_t)n_v * per_v;
   const int64_t items_m = a.valu_takes_m ? (int64_t)n_m * per_m : 0;
   const int64_t per_grp = items_v + items_m;
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   // item begins without a round trip to memory.
   struct Ahead {
     lora_problem pr;
-    int tile, q, word;  // tile, item within the tile (slice and chunk), record word
+    int tile, q, word, sb;  // tile, item within the tile (slice and chunk), record word, row block
     bool is_m;
   };
   auto load_ahead = [&](int64_t it, Ahead &h) {
@@ -330,6 +334,11 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     const int per = h.is_m ? per_m : per_v;
     h.tile = int(rem / per);
     h.q = int(rem - (int64_t)h.tile * per);
+    h.sb = 0;
+    if (h.is_m) {  // an MFMA-sized tile: row block, then slice and chunk
+      h.sb = h.q / a.cmo[a.ns];
+      h.q -= h.sb * a.cmo[a.ns];
+    }
     const int slice = chunk_of(a, h.is_m, h.q).slice;
     h.pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + slice) : a.single;
     h.word = 0;
@@ -347,16 +356,17 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     if (nx >= 0) load_ahead(nx, nxt);
     const Chunk c = chunk_of(a, cur.is_m, cur.q);
     const int o_lo = c.o_lo, o_hi = c.o_hi;
-    int nrows;
+    int row_lo = 0, row_hi;
     if (cur.is_m) {
       const int4 td = gload<int4>(a.tiles_m + cur.tile);
       setup_rows(a, td, n_active, M);
-      nrows = td.z;
+      row_lo = cur.sb * kRowBlock;
+      row_hi = min(td.z, row_lo + kRowBlock);
     } else {
-      nrows = setup_from_record(a, cur.word, M);
+      row_hi = setup_from_record(a, cur.word, M);
     }
-    if (M.nact > 0 && (MODE == MODE_SHRINK || o_lo < o_hi))
-      valu_tile<T, VEC, MODE>(a, cur.pr, nrows, o_lo, o_hi, c.d_out, M, s_v);
+    if (M.nact > 0 && row_lo < row_hi && (MODE == MODE_SHRINK || o_lo < o_hi))
+      valu_tile<T, VEC, MODE>(a, cur.pr, row_lo, row_hi, o_lo, o_hi, c.d_out, M, s_v);
     __syncthreads();
     it = nx;
     i += per_xcd;
