@@ -347,16 +347,21 @@ __device__ inline Chunk chunk_of(const ApplyArgs &a, bool is_m, int q) {
 
 // Work items are (group, tile, slice, output chunk), in that order: the
 // slices of a group that read one x take a tile's x in consecutive items.
-// Items are dealt round-robin over the workgroups, and so over the XCDs
-// (blockIdx % 8 is the XCD a workgroup is dispatched to): tiles of very
-// different cost (a request with three stacked adapters runs three shrink
-// and expand passes) sit next to each other in the plan's order, and
-// contiguous ranges per XCD left a few XCDs with all the long tiles.  The
-// adapter a group's tiles share is then staged from each XCD's L2 (or the
-// shared cache behind them) rather than one.
+// The items of one tile (every slice and chunk: `per_unit` of them) form a
+// unit; units are dealt round-robin over the XCDs (blockIdx % 8 is the XCD
+// a workgroup is dispatched to) and an XCD's workgroups take its units' items
+// in order.  Round-robin, because tiles of very different cost (a request
+// with three stacked adapters runs three shrink and expand passes) sit next
+// to each other in the plan's order and contiguous ranges per XCD left a few
+// XCDs with all the long tiles; whole units, so that the slices and chunks of
+// a tile share one L2 (and its x).
 template <class F>
-__device__ inline void walk_items(int64_t n_items, F &&body) {
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+__device__ inline void walk_items(int64_t n_items, int per_unit, F &&body) {
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+  for (int64_t k = lb;; k += per_xcd) {
+    const int64_t unit = xcd + 8 * (k / per_unit);
+    const int64_t item = unit * per_unit + k % per_unit;
+    if (item >= n_items) break;
     body(item);
     __syncthreads();
   }

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
   const int n_chunks = (d_out + kStepRows * kStepsPerItem - 1) / (kStepRows * kStepsPerItem);
   const int64_t per_prob = (int64_t)a.n_strips * n_chunks;
 
-  walk_items(per_prob * a.n_problems, [&](int64_t item) {
+  walk_items(per_prob * a.n_problems, 1, [&](int64_t item) {
     const int p = int(item / per_prob);
     const int64_t rem = item - (int64_t)p * per_prob;
     const int strip = int(rem / n_chunks), chunk = int(rem % n_chunks);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void merge_valu_kernel(MergeArgs a) {
   const int n_strips = (d_in + kValuCols - 1) / kValuCols;
   const int n_chunks = (d_out + kValuRowsPerItem - 1) / kValuRowsPerItem;
   const int64_t per_prob = (int64_t)n_strips * n_chunks;
-  walk_items(per_prob * a.n_problems, [&](int64_t item) {
+  walk_items(per_prob * a.n_problems, 1, [&](int64_t item) {
     const int p = int(item / per_prob);
     const int64_t rem = item - (int64_t)p * per_prob;
     const int strip = int(rem / n_chunks), chunk = int(rem % n_chunks);

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
   const int n_m = small ? n_ms : n_m64;
   const int4 *tiles = small ? a.tiles_ms : a.tiles_m;
   const int64_t per_grp = (int64_t)n_m * per_tile;
-  walk_items(per_grp * a.n_problems, [&](int64_t item) {
+  walk_items(per_grp * a.n_problems, per_tile, [&](int64_t item) {
     const int g = int(item / per_grp);
     const int64_t rem = item - (int64_t)g * per_grp;
     // tiles in reverse plan order: the plan puts the requests with several
