@@ -334,6 +334,9 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     const int per = h.is_m ? per_m : per_v;
     h.tile = int(rem / per);
     h.q = int(rem - (int64_t)h.tile * per);
+    // tiles in reverse plan order: requests with several adapters (the
+    // longest tiles) come last in the plan and should start first
+    h.tile = (h.is_m ? n_m : n_v) - 1 - h.tile;
     h.sb = 0;
     if (h.is_m) {  // an MFMA-sized tile: row block, then slice and chunk
       h.sb = h.q / a.cmo[a.ns];
