@@ -19,11 +19,17 @@
 //   3. counting sort of requests by key (histogram, scan, scatter);
 //   4. prefix sums of the sorted requests' lengths (rows in sorted order);
 //   5. group boundaries; a group of >= kMfmaMinRows rows is cut into MFMA
-//      tiles of kMfmaRows rows, a smaller one into VALU tiles of kValuRows;
-//   6. one tile descriptor per tile: {first row, first request, rows, group end},
-//      and for VALU tiles a record with each row's token row and request and
-//      the tile's compacted adapters, so the apply kernels start streaming
-//      after one read (two with per-slot scales).
+//      tiles of kMfmaRows rows, and a second time into tiles of
+//      kMfmaRowsSmall rows (the MFMA kernel picks one tiling per launch), a
+//      smaller group into VALU tiles of kValuRows;
+//   6. one tile descriptor per tile.  An MFMA tile inside one request:
+//      {first row, request, rows, first token row}; one that spans requests:
+//      {first row, first sorted request, rows, -1}.  A VALU tile: {first row,
+//      first sorted request, rows, group end}, and a record with each row's
+//      token row and request and the tile's compacted adapters, so the apply
+//      kernels start streaming after one read (two with per-slot scales).
+// The one-wave kernel (batches of up to 64 requests) takes the same steps
+// with wave scans and a rank sort instead of the counting sort.
 // Rows never move: a tile names rows by (sorted request, offset) and the apply
 // kernels read and write x / y rows in place.
 
