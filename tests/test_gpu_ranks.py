@@ -111,3 +111,52 @@ def test_ranks_in_multi_launch_and_merge(orc):
         c = W.Case(f"multi{q}", W.BF16, batch, base, xs[q], ys[q])
         y_ref, touched, _, _ = orc.apply_case(c, ranks=ranks)
         assert_parity(c, from_dev(yd[q], W.BF16), y_ref, touched, what=f"multi problem {q}")
+
+
+def test_ranks_decode_full_size_sampled(orc):
+    """The mixed-rank decode as it is timed: rank-64 pools of 1000 4096 x 4096
+    adapters whose ranks are 8, 16, 32 or 64, the 64-token Zipf batch, several
+    layers in one multi-problem launch with the pool's rank array.  Every
+    element past an adapter's rank is NaN; two layers are checked in full
+    against the oracle (on the adapters the batch uses)."""
+    layers, n, r, d = 4, 1000, 64, 4096
+    ranks_np = np.random.default_rng(W.SEEDS["C2"]).choice([8, 16, 32, 64], size=n).astype(np.int32)
+    ranks = torch.from_numpy(ranks_np).to(DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(W.SEEDS["C2"] + 7)
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(shape, generator=gen, device=DEV) * std).to(torch.bfloat16)
+
+    live_rows = torch.arange(r, device=DEV)[None, :] < ranks[:, None]  # [n][r]
+    pools = []
+    for _ in range(layers):
+        A, B = rnd(n, r, d, std=0.02), rnd(n, d, r, std=0.02)
+        A.masked_fill_(~live_rows[:, :, None], float("nan"))
+        B.masked_fill_(~live_rows[:, None, :], float("nan"))
+        pools.append((A, B))
+    xs = [rnd(64, d) for _ in range(layers)]
+    y0 = [rnd(64, d) for _ in range(layers)]
+    ys = [y.clone() for y in y0]
+    batch = W.batch_c2(np.random.default_rng(W.SEEDS["C2"]), n)
+    db = dev_batch(batch)
+    plan = L.new_workspace(db, n, DEV)
+    L.lora_plan_build(db, n, plan)
+    table, aligned = L.problems_table([(A, B, x, y) for (A, B), x, y in zip(pools, xs, ys)], DEV)
+    assert aligned
+    L.lora_apply_multi(L.Pool(pools[0][0], pools[0][1], ranks), db, plan, table, aligned)
+    torch.cuda.synchronize()
+    used = np.unique(batch.idx[batch.idx >= 0])
+    remap = np.full(n, -1, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    idx_small = np.where(batch.idx >= 0, remap[np.maximum(batch.idx, 0)], -1).astype(np.int32)
+    sel = torch.from_numpy(used.astype(np.int64)).to(DEV)
+    for li in (0, layers - 1):
+        assert not torch.isnan(ys[li].float()).any(), f"layer {li}: the padding past a rank was read"
+        A_s = from_dev(torch.nan_to_num(pools[li][0][sel], nan=0.0), W.BF16)
+        B_s = from_dev(torch.nan_to_num(pools[li][1][sel], nan=0.0), W.BF16)
+        pool = W.Pool(W.BF16, len(used), r, d, d, A_s, B_s)
+        small = W.Batch(64, 64, 1, None, idx_small, None)
+        case = W.Case(f"ranks_decode_layer{li}", W.BF16, small, pool, from_dev(xs[li], W.BF16), from_dev(y0[li], W.BF16))
+        y_ref, touched, _, _ = orc.apply_case(case, ranks=ranks_np[used])
+        assert_parity(case, from_dev(ys[li], W.BF16), y_ref, touched, what=case.name)
