@@ -348,18 +348,25 @@ __device__ inline Chunk chunk_of(const ApplyArgs &a, bool is_m, int q) {
 // Work items are (group, tile, slice, output chunk), in that order: the
 // slices of a group that read one x take a tile's x in consecutive items.
 // The items of one tile (every slice and chunk: `per_unit` of them) form a
-// unit; units are dealt round-robin over the XCDs (blockIdx % 8 is the XCD
-// a workgroup is dispatched to) and an XCD's workgroups take its units' items
-// in order.  Round-robin, because tiles of very different cost (a request
-// with three stacked adapters runs three shrink and expand passes) sit next
-// to each other in the plan's order and contiguous ranges per XCD left a few
-// XCDs with all the long tiles; whole units, so that the slices and chunks of
-// a tile share one L2 (and its x).
+// unit; blocks of up to kUnitBlock consecutive units (fewer when the launch
+// has too few units for about eight blocks per XCD) are dealt round-robin over the
+// XCDs (blockIdx % 8 is the XCD a workgroup is dispatched to), and an XCD's
+// workgroups take its blocks' items in order.  Round-robin, because tiles of
+// very different cost (a request with three stacked adapters runs three
+// shrink and expand passes) sit next to each other in the plan's order and
+// contiguous ranges per XCD left a few XCDs with all the long tiles; blocks of
+// consecutive tiles, because those mostly share an adapter, which an XCD then
+// stages into its L2 once per block rather than once per tile; whole units, so
+// that the slices and chunks of a tile share one L2 (and its x).
+constexpr int kUnitBlock = 8;
 template <class F>
 __device__ inline void walk_items(int64_t n_items, int per_unit, F &&body) {
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+  const int64_t n_units = (n_items + per_unit - 1) / per_unit;
+  const int blk = (int)min<int64_t>(kUnitBlock, max<int64_t>(1, n_units / 64));
   for (int64_t k = lb;; k += per_xcd) {
-    const int64_t unit = xcd + 8 * (k / per_unit);
+    const int64_t u = k / per_unit;  // the XCD's u-th unit
+    const int64_t unit = (xcd + 8 * (u / blk)) * blk + u % blk;
     const int64_t item = unit * per_unit + k % per_unit;
     if (item >= n_items) break;
     body(item);
