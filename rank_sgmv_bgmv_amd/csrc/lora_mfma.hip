@@ -21,10 +21,7 @@
 //     the expand's v_mfma_f32_16x16x16_bf16.  Each lane parks them in LDS
 //     (its own row, read back only by itself) until the expand.
 //   Expand: Y^T[o][t] += sum_j B[o][j] v[t][j] per stage of 128 outputs (and
-//     per slot).  (A second build halves both stages -- d_in columns per
-//     shrink stage, outputs per expand stage -- for tiles with many stacked
-//     slots, whose parked intermediates would otherwise leave LDS for one
-//     workgroup per CU.)  B is staged through LDS with the next stage prefetched into
+//     per slot).  B is staged through LDS with the next stage prefetched into
 //     registers; y is read one stage ahead straight into the accumulator
 //     layout, added and rounded once to bf16, and written back.  The B rows
 //     of each pair of 16-wide output tiles are interleaved as they are staged
@@ -32,6 +29,10 @@
 //     row: y moves in 16-byte pieces.
 // Every bf16 product is exact in fp32 and accumulation is fp32; the rank-r
 // intermediate is rounded once to bf16 before the expand.
+//
+// A second build halves both stages (d_in columns per shrink stage, outputs
+// per expand stage) for tiles with many stacked slots, whose parked
+// intermediates would otherwise leave LDS for one workgroup per CU.
 
 #include "lora_device.hpp"
 
