@@ -177,3 +177,30 @@ def test_pool_load_validation(lib):
     assert lib.lora_pool_load(ctypes.byref(pool), -1, FAKE, FAKE, None) == -2
     assert lib.lora_pool_load(ctypes.byref(pool), 0, None, FAKE, None) == -1
     assert lib.lora_pool_load(ctypes.byref(_pool(A=None)), 0, FAKE, FAKE, None) == -1
+
+
+def test_sliced_table_layout_and_checks():
+    """The binding's table for lora_apply_sliced (host-side marshalling only):
+    group-major rows of (A, B, x, y, ldx, ldy), the slices' widths, and the
+    errors it raises before anything reaches the library."""
+    import torch
+    n, r, d_in, T = 3, 8, 64, 5
+    x = torch.zeros((T, d_in + 8), dtype=torch.bfloat16)[:, :d_in]
+
+    def slice_(d_out):
+        return (torch.zeros((n, r, d_in), dtype=torch.bfloat16), torch.zeros((n, d_out, r), dtype=torch.bfloat16),
+                torch.zeros((T, d_out), dtype=torch.bfloat16))
+
+    g0, g1 = [slice_(32), slice_(16)], [slice_(32), slice_(16)]
+    table, d_outs, aligned = L.sliced_table([(x, g0), (x, g1)], "cpu")
+    assert d_outs == [32, 16] and aligned
+    assert tuple(table.shape) == (4, 6)
+    rows = table.tolist()
+    for i, (A, B, y) in enumerate(g0 + g1):
+        assert rows[i][:4] == [A.data_ptr(), B.data_ptr(), x.data_ptr(), y.data_ptr()]
+        assert rows[i][4:] == [d_in + 8, y.shape[1]]
+    with pytest.raises(L.LoraError):
+        L.sliced_table([(x, [slice_(32), slice_(16)]), (x, [slice_(32), slice_(24)])], "cpu")
+    shape = L.Pool(*g0[0][:2])
+    with pytest.raises(L.LoraError):  # 4 rows are not whole groups of 3 slices
+        L.lora_apply_sliced(shape, None, None, table, [32, 16, 16])
