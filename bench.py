@@ -153,7 +153,8 @@ def result(name, wall, steps, tokens, bytes_step, flops_step, k_ms_avg, k_bytes,
 
 
 # ---------------------------------------------------------------- workloads --
-def bench_decode_layers(dev, steps, warmup, layers=32, n=1000, n_batches=16, seed=W.SEEDS["C2"]):
+def bench_decode_layers(dev, steps, warmup, layers=32, n=1000, n_batches=16, seed=W.SEEDS["C2"],
+                        make_batch=W.batch_c2, name="decode q_proj"):
     """C2 batch through `layers` q_proj pools: plan + one multi-problem launch per step."""
     torch = torch_mod()
     import rank_sgmv_bgmv_amd as L
@@ -163,7 +164,7 @@ def bench_decode_layers(dev, steps, warmup, layers=32, n=1000, n_batches=16, see
     pools = [randn_pool(gen, n, r, d, d, dev) for _ in range(layers)]
     xs = [randn_act(gen, 64, d, dev) for _ in range(layers)]
     ys = [randn_act(gen, 64, d, dev) for _ in range(layers)]
-    batches = [W.batch_c2(np.random.default_rng([seed, j]), n) for j in range(n_batches)]
+    batches = [make_batch(np.random.default_rng([seed, j]), n) for j in range(n_batches)]
     dbs = [dev_batch(b, dev) for b in batches]
     plan = L.new_workspace(dbs[0], n, dev)
     shape = L.Pool(pools[0][0], pools[0][1])
@@ -180,10 +181,11 @@ def bench_decode_layers(dev, steps, warmup, layers=32, n=1000, n_batches=16, see
     tm = Timer(steps)
     wall, k_ms, _ = tm.run(step, warmup)
     used = [batches[i % n_batches] for i in range(steps)]
-    distinct = np.mean([len(np.unique(b.idx)) for b in used])
+    distinct = np.mean([len(np.unique(b.idx[b.idx >= 0])) for b in used])
+    slot_tokens = np.mean([int((b.idx >= 0).sum()) for b in used])
     k_bytes = layers * accounting.call_bytes(64, distinct, r, d, d, 2)
-    k_flops = layers * accounting.lora_flops(64, r, d, d)
-    res = result(f"decode q_proj x{layers} layers", wall, steps, 64, k_bytes, k_flops, k_ms, k_bytes, k_flops, 1,
+    k_flops = layers * accounting.lora_flops(slot_tokens, r, d, d)
+    res = result(f"{name} x{layers} layers", wall, steps, 64, k_bytes, k_flops, k_ms, k_bytes, k_flops, 1,
                  {"distinct_adapters_per_layer": float(distinct), "layers": layers})
     return res, (pools, batches, xs, ys)
 
@@ -546,7 +548,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c4x,c5,merge,ranks,poolload")
+    ap.add_argument("--only", default="", help="comma list of: decode32,c1,c2,c3,c4,c4x,c5,merge,stacked,ranks,poolload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (the reference kernel for HBM byte counters)")
@@ -595,6 +597,12 @@ def main():
         modes = tuple(m for m in ("multi", "sliced") if os.environ.get("LORA_BENCH_C4X_MODE", m) == m)
         variants["C4_llama3_8b_shared_x"] = bench_c4_shared_x(dev, max(3, args.steps // 4), max(1, args.warmup // 2),
                                                               modes=modes)
+    if want("stacked"):
+        log("decode stacked ...")
+        torch.cuda.empty_cache()
+        variants["decode_stacked_x32"], _ = bench_decode_layers(
+            dev, args.steps, args.warmup, make_batch=W.batch_decode_stacked,
+            name="decode q_proj, 30% of requests stacking 2-3 adapters,")
     if want("ranks"):
         log("ranks ...")
         torch.cuda.empty_cache()

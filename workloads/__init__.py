@@ -211,6 +211,19 @@ def batch_c2(rng, n=1000, T=64) -> Batch:
     return Batch(T, T, 1, None, idx, None)
 
 
+def batch_decode_stacked(rng, n=1000, T=64, K=3) -> Batch:
+    """The C2 decode batch with C5's stacking: one token per request, and
+    round(0.3*T) requests, chosen at random, stack 2 or 3 distinct adapters;
+    every adapter drawn Zipf(1.1) over the pool."""
+    z = ZipfAdapters(rng, n, 1.1)
+    idx = np.full((T, K), -1, dtype=np.int32)
+    stacked = set(int(s) for s in rng.choice(T, size=int(round(0.3 * T)), replace=False))
+    for s in range(T):
+        k = int(rng.integers(2, 4)) if s in stacked else 1
+        idx[s, :k] = z.draw_distinct(rng, k)
+    return Batch(T, T, K, None, idx, None)
+
+
 def case_c2(seed: int = SEEDS["C2"], n: int = 1000) -> Case:
     rng = np.random.default_rng(seed)
     batch = batch_c2(rng, n)
