@@ -250,6 +250,45 @@ def test_decode_x32_multi_sampled(orc):
         assert_parity(case, from_dev(ys[li], W.BF16), y_ref, touched, what=case.name)
 
 
+def test_decode_stacked_multi_sampled(orc):
+    """The stacked decode launch as it is timed: 64 one-token requests, 30% of
+    them stacking 2-3 Zipf adapters, rank-16 4096 x 4096 pools of 1000
+    adapters, several layers in one multi-problem launch; two layers checked
+    in full against the oracle (on the adapters the batch uses)."""
+    layers, n, r, d = 4, 1000, 16, 4096
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(W.SEEDS["C2"] + 11)
+    batch = W.batch_decode_stacked(np.random.default_rng([W.SEEDS["C2"], 0]), n)
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(shape, generator=gen, device=DEV) * std).to(torch.bfloat16)
+
+    pools = [(rnd(n, r, d, std=0.02), rnd(n, d, r, std=0.02)) for _ in range(layers)]
+    xs = [rnd(64, d) for _ in range(layers)]
+    y0 = [rnd(64, d) for _ in range(layers)]
+    ys = [y.clone() for y in y0]
+    db = dev_batch(batch)
+    plan = L.new_workspace(db, n, DEV)
+    L.lora_plan_build(db, n, plan)
+    table, aligned = L.problems_table([(A, B, x, y) for (A, B), x, y in zip(pools, xs, ys)], DEV)
+    assert aligned
+    L.lora_apply_multi(L.Pool(*pools[0]), db, plan, table, aligned)
+    torch.cuda.synchronize()
+    used = np.unique(batch.idx[batch.idx >= 0])
+    remap = np.full(n, -1, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    idx_small = np.where(batch.idx >= 0, remap[np.maximum(batch.idx, 0)], -1).astype(np.int32)
+    sel = torch.from_numpy(used.astype(np.int64)).to(DEV)
+    for li in (0, layers - 1):
+        A_s, B_s = from_dev(pools[li][0][sel], W.BF16), from_dev(pools[li][1][sel], W.BF16)
+        pool = W.Pool(W.BF16, len(used), r, d, d, A_s, B_s)
+        small = W.Batch(64, 64, batch.K, None, idx_small, None)
+        case = W.Case(f"decode_stacked_layer{li}", W.BF16, small, pool, from_dev(xs[li], W.BF16),
+                      from_dev(y0[li], W.BF16))
+        y_ref, touched, _, _ = orc.apply_case(case)
+        assert_parity(case, from_dev(ys[li], W.BF16), y_ref, touched, what=case.name)
+
+
 def _c4_layer(layer_seed=0):
     """One layer of the Llama-3-8B-shaped stack: the batch (shared) and 7 projection cases."""
     rng = np.random.default_rng(W.SEEDS["C4"])
