@@ -27,9 +27,12 @@
  *
  * Memory and ownership.  Every pointer in a struct or argument below is a
  * DEVICE pointer unless its comment says "host".  All buffers are allocated
- * and owned by the caller; the library allocates and frees nothing, keeps no
- * global state and is re-entrant.  Every compute call is asynchronous on the
- * given stream and never synchronizes, except lora_read_device_errors.
+ * and owned by the caller; the library allocates and frees nothing and is
+ * re-entrant.  The only state it keeps between calls is looked up once and
+ * never changes: each device's compute-unit count, the kernels' LDS limit,
+ * and the tuning values read from the environment at the first call.  Every
+ * compute call is asynchronous on the given stream and never synchronizes,
+ * except lora_read_device_errors.
  * x and y must not overlap; v must overlap neither x nor y.
  *
  * Errors.  Problems visible on the host (NULL pointers, non-positive sizes,
