@@ -192,6 +192,28 @@ def test_c3_prefill_sampled(orc):
     assert_parity(case, out, y_ref, touched, rows=rows, what="C3")
 
 
+def test_c3_stacked_sampled(orc):
+    """C3's lengths and pools with a third of the requests stacking a second,
+    scaled adapter and one request with none: the long groups take the 48-row
+    prefill tiling, with tiles that span requests and tiles with two slots."""
+    base = W.case_c3()
+    rng = np.random.default_rng(9103)
+    S = base.batch.S
+    idx = np.full((S, 2), -1, np.int32)
+    idx[:, 0] = base.batch.idx[:, 0]
+    for s in rng.choice(S, size=S // 3, replace=False):
+        idx[s, 1] = (idx[s, 0] + 1 + int(rng.integers(0, 7))) % base.pool.n
+    idx[int(rng.integers(0, S)), :] = -1
+    scale = rng.uniform(0.5, 1.5, (S, 2)).astype(np.float32)
+    batch = W.Batch(base.batch.T, S, 2, base.batch.seg_off, idx, scale)
+    case = W.Case("C3_stacked", W.BF16, batch, base.pool, base.x, base.y)
+    out = DevCase(case).apply()
+    rows = sample_rows(batch, 64, 4)
+    y_ref, touched, _, _ = orc.apply_case(case, rows=rows)
+    assert not touched.all(), "the request with no adapter must stay untouched"
+    assert_parity(case, out, y_ref, touched, rows=rows, what="C3 stacked")
+
+
 @pytest.mark.parametrize("d,r", [(1280, 64), (1280, 128), (640, 64), (640, 128)])
 def test_c5_diffusion_sampled(orc, d, r):
     case = W.case_c5(d, r)
