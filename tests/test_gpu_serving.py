@@ -124,3 +124,49 @@ def test_scale_schedule_reuses_the_plan(orc):
         c = W.Case(f"step{step}", W.BF16, W.Batch(b.T, b.S, b.K, b.seg_off, b.idx, sc), p, case.x, case.y)
         y_ref, touched, _, _ = orc.apply_case(c)
         assert_parity(c, from_dev(y, W.BF16), y_ref, touched, what=f"schedule step {step} (w={w})")
+
+
+def test_next_plan_built_on_a_second_stream(orc):
+    """A decode loop that builds the plan of step j + 1 on a second stream,
+    into the other of two workspaces, while step j's launch runs over three
+    layers; events order each plan before its launch and each workspace's
+    reuse after the launch that read it.  Every step's outputs match the
+    oracle."""
+    n, r, d, layers, steps = 60, 16, 512, 3, 6
+    rng = np.random.default_rng(4400)
+    pool_np = [W.make_pool(rng, W.BF16, n, r, d, d, 0.02) for _ in range(layers)]
+    pools = [(to_dev(p.A, W.BF16), to_dev(p.B, W.BF16)) for p in pool_np]
+    shape = L.Pool(*pools[0])
+    batches = [W.batch_c2(np.random.default_rng([4400, j]), n) for j in range(steps)]
+    dbs = [dev_batch(b) for b in batches]
+    xy = [[W.make_xy(rng, W.BF16, b.T, d, d, None, None) for _ in range(layers)] for b in batches]
+    ys = [[to_dev(y, W.BF16) for _, y in s] for s in xy]
+    xs = [[to_dev(x, W.BF16) for x, _ in s] for s in xy]
+    tables = [L.problems_table([(A, B, x, y) for (A, B), x, y in zip(pools, xs[j], ys[j])], DEV)[0]
+              for j in range(steps)]
+    plans = [L.new_workspace(dbs[0], n, DEV) for _ in range(2)]
+    main = torch.cuda.current_stream(DEV)
+    side = torch.cuda.Stream(device=DEV)
+    planned = [torch.cuda.Event() for _ in range(2)]
+    consumed = [torch.cuda.Event() for _ in range(2)]
+
+    def build(j):
+        with torch.cuda.stream(side):
+            side.wait_event(consumed[j % 2])
+            L.lora_plan_build(dbs[j], n, plans[j % 2])
+            planned[j % 2].record(side)
+
+    build(0)
+    for j in range(steps):
+        main.wait_event(planned[j % 2])
+        L.lora_apply_multi(shape, dbs[j], plans[j % 2], tables[j])
+        consumed[j % 2].record(main)
+        if j + 1 < steps:
+            build(j + 1)
+    torch.cuda.synchronize()
+    for j, b in enumerate(batches):
+        for li, p in enumerate(pool_np):
+            x, y = xy[j][li]
+            c = W.Case(f"step{j}_layer{li}", W.BF16, b, p, x, y)
+            y_ref, touched, _, _ = orc.apply_case(c)
+            assert_parity(c, from_dev(ys[j][li], W.BF16), y_ref, touched, what=f"step {j} layer {li}")
