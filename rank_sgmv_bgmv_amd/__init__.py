@@ -169,6 +169,31 @@ def _ld(t) -> int:
     return int(t.stride(0))
 
 
+def _same_device(what: str, dev, *tensors):
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise LoraError(-1, f"{what}: every tensor must be on {dev} (found {t.device})")
+
+
+def _check_rows(what: str, pool: "Pool", batch: Batch, x=None, y=None, v=None, ws=None):
+    """Shapes, dtypes and devices of one call's tensors against its pool and batch:
+    x [>= T][>= d_in] and y [>= T][>= d_out] of the pool's dtype, v float32
+    [>= T][>= K*r], everything (batch tensors included) on the pool's device."""
+    torch = _torch()
+    dev = pool.A.device
+    if dev.type != "cuda":
+        raise LoraError(-1, f"{what}: the pool must be in device memory")
+    _same_device(what, dev, pool.B, pool.ranks, batch.idx, batch.seg_off, batch.scale, x, y, v, ws)
+    for name, t, cols, dt in (("x", x, pool.d_in, pool.A.dtype), ("y", y, pool.d_out, pool.A.dtype),
+                              ("v", v, batch.K * pool.r, torch.float32)):
+        if t is None:
+            continue
+        if t.dim() != 2 or t.shape[0] < batch.T or t.shape[1] < cols:
+            raise LoraError(-2, f"{what}: {name} must be at least [{batch.T}][{cols}] (got {tuple(t.shape)})")
+        if t.dtype != dt:
+            raise LoraError(-2, f"{what}: {name} must be {dt} (got {t.dtype})")
+
+
 def lora_workspace_size(batch: Batch, n_adapters: int) -> int:
     return int(lib().lora_workspace_size(ctypes.byref(batch.c), n_adapters))
 
@@ -182,36 +207,43 @@ def new_workspace(batch: Batch, n_adapters: int, device):
 
 
 def lora_plan_build(batch: Batch, n_adapters: int, plan):
+    _same_device("lora_plan_build", plan.device, batch.idx, batch.seg_off, batch.scale)
     _check(lib().lora_plan_build(ctypes.byref(batch.c), n_adapters, _ptr(plan), plan.numel(), _stream(plan)),
            "lora_plan_build")
 
 
 def lora_apply(pool: Pool, batch: Batch, x, y, ws):
+    _check_rows("lora_apply", pool, batch, x=x, y=y, ws=ws)
     _check(lib().lora_apply(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(x), _ld(x), _ptr(y), _ld(y), _ptr(ws),
                             ws.numel(), _stream(y)), "lora_apply")
 
 
 def lora_shrink(pool: Pool, batch: Batch, x, v, ws):
+    _check_rows("lora_shrink", pool, batch, x=x, v=v, ws=ws)
     _check(lib().lora_shrink(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(x), _ld(x), _ptr(v), _ld(v),
                              _ptr(ws), ws.numel(), _stream(v)), "lora_shrink")
 
 
 def lora_expand(pool: Pool, batch: Batch, v, y, ws):
+    _check_rows("lora_expand", pool, batch, y=y, v=v, ws=ws)
     _check(lib().lora_expand(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(v), _ld(v), _ptr(y), _ld(y),
                              _ptr(ws), ws.numel(), _stream(y)), "lora_expand")
 
 
 def lora_apply_planned(pool: Pool, batch: Batch, plan, x, y):
+    _check_rows("lora_apply_planned", pool, batch, x=x, y=y, ws=plan)
     _check(lib().lora_apply_planned(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), _ptr(x),
                                     _ld(x), _ptr(y), _ld(y), _stream(y)), "lora_apply_planned")
 
 
 def lora_shrink_planned(pool: Pool, batch: Batch, plan, x, v):
+    _check_rows("lora_shrink_planned", pool, batch, x=x, v=v, ws=plan)
     _check(lib().lora_shrink_planned(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), _ptr(x),
                                      _ld(x), _ptr(v), _ld(v), _stream(v)), "lora_shrink_planned")
 
 
 def lora_expand_planned(pool: Pool, batch: Batch, plan, v, y):
+    _check_rows("lora_expand_planned", pool, batch, y=y, v=v, ws=plan)
     _check(lib().lora_expand_planned(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), _ptr(v),
                                      _ld(v), _ptr(y), _ld(y), _stream(y)), "lora_expand_planned")
 
@@ -234,6 +266,8 @@ def problems_table(problems: Sequence, device):
 def lora_apply_multi(shape: Pool, batch: Batch, plan, table, aligned: bool = True):
     """shape: a Pool whose shape (n, r, d_in, d_out, dtype) all problems share."""
     n = int(table.shape[0]) if table.numel() else 0
+    _check_rows("lora_apply_multi", shape, batch, ws=plan)
+    _same_device("lora_apply_multi", plan.device, table)
     _check(lib().lora_apply_multi(ctypes.byref(shape.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), n,
                                   _ptr(table), 1 if aligned else 0, _stream(plan)), "lora_apply_multi")
 
@@ -263,6 +297,8 @@ def lora_apply_sliced(shape: Pool, batch: Batch, plan, table, d_outs: Sequence[i
     if ns < 1 or rows % ns:
         raise LoraError(-2, "table rows must be a whole number of groups of len(d_outs) slices")
     widths = (ctypes.c_int32 * ns)(*[int(v) for v in d_outs])
+    _check_rows("lora_apply_sliced", shape, batch, ws=plan)
+    _same_device("lora_apply_sliced", plan.device, table)
     _check(lib().lora_apply_sliced(ctypes.byref(shape.c), ctypes.byref(batch.c), _ptr(plan), plan.numel(), rows // ns,
                                    ns, widths, _ptr(table), 1 if aligned else 0, _stream(plan)), "lora_apply_sliced")
 

@@ -1,12 +1,13 @@
 """Algorithmic work of one unmerged multi-LoRA call: bytes and FLOPs.
 
 These counts define what a launch *must* move and compute; they are what the
-benchmark divides by measured time.  They restate the cost model of
-"Serving several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
-alongside" (the ``lora_costs`` function and its printed FLUX table), which
-counts 2 N (d r + r d) extra FLOPs per adapted layer and d r 2 elements per
-LoRA, generalised to A: r x d_in, B: d_out x r.  The page's table is pinned in
-tests/golden/lora_costs_flux.txt.
+benchmark divides by measured time.  They follow the cost model of "Serving
+several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
+alongside": the alongside form costs two multiply-add FLOPs per element of
+each of the two low-rank products, an adapter holds the elements of A and B,
+and merging (or unmerging) reads and writes every affected weight once.  Here
+A is r x d_in and B is d_out x r.  The tests rebuild the page's printed FLUX
+table (tests/golden/lora_costs_flux.txt) from these functions.
 """
 from __future__ import annotations
 
@@ -53,14 +54,7 @@ def batch_work(seg_bounds: Iterable, idx, n_adapters: int):
     return touched, slot_tokens, len(used)
 
 
-def lora_costs(d_model: int, layers: int, adapted_per_layer: int, rank: int, n_tokens: int,
-               hbm_gbps: float = 3350.0, dtype: int = 2):
-    """The page's cost model for a square d x d model: (extra compute relative to the
-    adapted layers, merge-or-unmerge time in ms, size of the LoRA in MiB)."""
-    n_layers = adapted_per_layer * layers
-    base = 2 * n_tokens * d_model * d_model * n_layers
-    extra = lora_flops(n_tokens, rank, d_model, d_model) * n_layers
-    weight_bytes = d_model * d_model * dtype * n_layers
-    merge_ms = 2 * weight_bytes / (hbm_gbps * 1e9) * 1e3
-    lora_mib = adapter_bytes(rank, d_model, d_model, dtype) * n_layers / 2 ** 20
-    return extra / base, merge_ms, lora_mib
+def merge_bytes(n_weights: int, d_out: int, d_in: int, elem: int) -> int:
+    """Weight traffic of merging (or unmerging) adapters into n_weights weights of
+    d_out x d_in: each weight is read once and written once."""
+    return 2 * n_weights * d_out * d_in * elem

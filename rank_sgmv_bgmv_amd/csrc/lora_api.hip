@@ -210,6 +210,8 @@ void fill_common(ApplyArgs &a, const lora_batch *b, const BatchDims &d, const Pl
   a.idx = b->idx;
   a.scale = b->scale;
   a.K = d.K;
+  a.T = d.T;
+  a.S = d.S;
   a.hdr = P.V.hdr;
   a.sseg = P.V.sseg;
   a.sst = P.V.sst;

@@ -175,6 +175,31 @@ template <> struct VOps<float, false> {
   static __device__ __forceinline__ void add_store(float *p, const float *d) { gstore(p, gload<float>(p) + d[0]); }
 };
 
+// ------------------------------------------------------------- plan header --
+// The header of the plan a launch uses, checked against the call.  A plan
+// built for another batch shape or pool size (or a workspace no plan was built
+// into) lays its arrays out at other offsets, so its tile descriptors would be
+// read from the wrong places: on a mismatch the kernel does no work at all and
+// workgroup 0 adds one to the plan's error word.
+struct PlanHdr {
+  int n_m, n_v, n_active, n_ms;
+  bool ok;
+};
+__device__ inline PlanHdr read_plan_header(const ApplyArgs &a) {
+  const int4 w0 = gload<int4>(a.hdr), w1 = gload<int4>(a.hdr + 4), w2 = gload<int4>(a.hdr + 8);
+  static_assert(H_TILES_M == 0 && H_TILES_V == 1 && H_ACTIVE == 3 && H_N == 6 && H_S == 7 && H_T == 8 &&
+                    H_K == 9 && H_MAGIC == 10 && H_TILES_MS == 11,
+                "header words read as three 16-byte pieces");
+  PlanHdr h;
+  h.n_m = w0.x;
+  h.n_v = w0.y;
+  h.n_active = w0.w;
+  h.n_ms = w2.w;
+  h.ok = w2.z == kPlanMagic && w1.z == a.n && w1.w == a.S && w2.x == a.T && w2.y == a.K;
+  if (!h.ok && blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(const_cast<int *>(a.hdr) + H_ERR, 1);
+  return h;
+}
+
 // ------------------------------------------------------------ tile metadata --
 constexpr int kMetaRows = kMfmaRows;  // rows of tile metadata
 struct Meta {

@@ -141,7 +141,8 @@ struct ApplyArgs {
   const int *idx;
   const float *scale;
   int K;
-  // plan (read only)
+  int T, S;  // the call's rows and requests (checked against the plan's header)
+  // plan (read only but for the error word)
   const int *hdr, *sseg, *sst, *cumlen;
   const int4 *tiles_m, *tiles_v;
   const int4 *tiles_ms;  // the plan's second MFMA tiling (kMfmaRowsSmall rows per tile)

@@ -5,8 +5,8 @@
 // is d_out x r), stacked LoRAs merge as a weighted sum (comparison table,
 // stacking row), and switching unmerges the old one and merges the new one --
 // one read and one write of the affected weights, which is the roofline the
-// page itself gives (its lora_costs listing: twice the weight bytes over the
-// HBM bandwidth).
+// page itself gives (its cost model: twice the weight bytes over the HBM
+// bandwidth).
 //
 // bf16: the update is a dense contraction of rank K*r, so it runs on the
 // matrix cores.  A workgroup owns a strip of kStripCols columns of W and walks

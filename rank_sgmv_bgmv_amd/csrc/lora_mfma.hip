@@ -271,8 +271,9 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
   Meta &M = *reinterpret_cast<Meta *>(smem);
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
   uint16_t *vpark = reinterpret_cast<uint16_t *>(smem + kMetaBytes + MfmaCfg<JT, HS>::LDS);
-  const int n_m64 = gload<int>(a.hdr + H_TILES_M), n_ms = gload<int>(a.hdr + H_TILES_MS);
-  const int n_active = gload<int>(a.hdr + H_ACTIVE);
+  const PlanHdr ph = read_plan_header(a);
+  if (!ph.ok) return;
+  const int n_m64 = ph.n_m, n_ms = ph.n_ms, n_active = ph.n_active;
   const int per_tile = a.cmo[a.ns];  // items of one tile, over every slice
   // The plan's 48-row tiling when the 64-row items are more than the CUs (so
   // some CUs would run two and set the launch's duration) but the 48-row items

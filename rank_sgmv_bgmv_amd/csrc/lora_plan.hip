@@ -211,6 +211,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
 
   if (tid == 0) s_err = 0;
   for (int b = tid; b <= n; b += kPlanThreads) cnt[b] = 0;
+  __syncthreads();  // the error word and the histogram are zero before any thread counts into them
 
   // 1. sanitised request starts, start[S] = end of the last request.
   if (P.per_token) {

@@ -295,8 +295,9 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Meta &M = *reinterpret_cast<Meta *>(smem);
   InterT<T, VEC, MODE> *s_v = reinterpret_cast<InterT<T, VEC, MODE> *>(smem + kMetaBytes);
-  const int n_m = gload<int>(a.hdr + H_TILES_M), n_v = gload<int>(a.hdr + H_TILES_V);
-  const int n_active = gload<int>(a.hdr + H_ACTIVE);
+  const PlanHdr ph = read_plan_header(a);
+  if (!ph.ok) return;
+  const int n_m = ph.n_m, n_v = ph.n_v, n_active = ph.n_active;
   // VALU tiles first; MFMA-sized tiles too when the MFMA kernel does not run,
   // each as kSubBlocks items of kRowBlock rows (one workgroup would otherwise
   // take a 64-row tile's row blocks one after another).  A tile's items run

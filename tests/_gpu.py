@@ -113,3 +113,26 @@ def sample_rows(batch: W.Batch, n_random: int, seed: int) -> np.ndarray:
     if batch.T:
         rows.update(int(v) for v in rng.integers(0, batch.T, size=n_random))
     return np.array(sorted(rows), dtype=np.int32)
+
+
+def check_problem_sampled(orc, batch: W.Batch, A, B, x, y0, y_out, rows, what, ranks=None):
+    """One problem of a large launch against the oracle on `rows`: the adapters
+    the batch uses are copied to the host (the oracle's result does not depend
+    on the others) and the batch's indices remapped to them.  A, B, x, y0 (y
+    before the launch) and y_out are device tensors of one dtype."""
+    dtype = W.BF16 if A.dtype == torch.bfloat16 else W.F32
+    n = int(A.shape[0])
+    idx = np.asarray(batch.idx)
+    used = np.unique(idx[(idx >= 0) & (idx < n)])
+    remap = np.full(n, -1, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    idx_small = np.where((idx >= 0) & (idx < n), remap[np.clip(idx, 0, n - 1)], -1).astype(np.int32)
+    sel = torch.from_numpy(used.astype(np.int64)).to(A.device)
+    pool = W.Pool(dtype, len(used), int(A.shape[1]), int(A.shape[2]), int(B.shape[1]),
+                  from_dev(A.index_select(0, sel), dtype), from_dev(B.index_select(0, sel), dtype))
+    small = W.Batch(batch.T, batch.S, batch.K, batch.seg_off, idx_small, batch.scale)
+    case = W.Case(what, dtype, small, pool, from_dev(x, dtype), from_dev(y0, dtype))
+    rk = None if ranks is None else np.asarray(ranks)[used]
+    y_ref, touched, _, _ = orc.apply_case(case, rows=rows, ranks=rk)
+    assert_parity(case, from_dev(y_out, dtype), y_ref, touched, rows=rows, what=what)
+    return touched

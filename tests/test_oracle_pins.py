@@ -24,14 +24,24 @@ def test_pin(orc, pin):
 
 
 def test_lora_costs_golden_table():
-    """The page's printed FLUX table is reproduced by the accounting used for bytes/FLOPs."""
+    """The page's printed FLUX table (57 layers x 4 adapted 3072 x 3072 attention
+    projections, 4608 tokens, 16-bit weights, 3350 GB/s) follows from the
+    accounting used for bytes and FLOPs: extra compute = the adapter's FLOPs over
+    the projections' own 2 N d^2; LoRA size = the adapters' bytes; merge time =
+    the merge's weight traffic over the bandwidth."""
     rows = [l.split() for l in open(os.path.join(GOLDEN, "lora_costs_flux.txt")) if l.strip() and not l.startswith("#")]
     assert len(rows) == 4
+    d, n_mats, tokens, elem, gbps = 3072, 57 * 4, 4608, 2, 3350.0
     for rank, extra_s, mb_s, ms_s in rows:
-        extra, merge_ms, mib = accounting.lora_costs(3072, 57, 4, int(rank), 4608)
+        r = int(rank)
+        extra = accounting.lora_flops(tokens, r, d, d) / (2 * tokens * d * d)
+        mib = n_mats * accounting.adapter_bytes(r, d, d, elem) / 2 ** 20
+        merge_ms = accounting.merge_bytes(n_mats, d, d, elem) / (gbps * 1e9) * 1e3
         assert f"{extra:.1%}" == extra_s
         assert f"{mib:.0f}" == mb_s
         assert f"{merge_ms:.0f}" == ms_s
+        # the same ratio in closed form: 2 r / d
+        assert abs(extra - 2 * r / d) < 1e-15
 
 
 def test_oracle_macs_match_accounting(orc):
