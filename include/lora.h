@@ -151,6 +151,24 @@ lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *w
 lora_status lora_apply(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
                        int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* lora_apply for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the plan built into a device array the
+ * library holds for the life of the process instead of a caller workspace.
+ * That array is LORA_NOALLOC_PLAN_BYTES (8 MiB) on every GPU the library runs
+ * on; a batch whose plan needs more (lora_workspace_size) is refused with
+ * LORA_EUNSUPPORTED before anything is launched (about 40 000 one-token
+ * requests, or segmented batches of up to about 60 000 rows and a few
+ * thousand requests, fit).  Nothing is allocated or freed, by the library or
+ * any routine it calls.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's plan: calls that may overlap on one GPU (two streams,
+ * or two host threads) race and must be ordered by the caller.  The stream
+ * must belong to the current device.  Errors as for lora_apply; the device
+ * error word is not readable for these calls. */
+#define LORA_NOALLOC_PLAN_BYTES (8u << 20)
+lora_status lora_apply_noalloc(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
+                               int64_t ldy, hipStream_t stream);
+
 /* Shrink half: v[t][k*rank + j] = scale[s][k] * sum_c x[t][c] A_i[j][c] for
  * every touched row t and slot k (zeros for a -1 slot of a touched row).
  * v: [T][ldv] float32, ldv >= max_slots*rank.  Rows that are not touched are

@@ -7,7 +7,7 @@ computation runs in the library's HIP kernels.  There is no CPU fallback: if
 the library has not been built, calls raise ``LoraError``.
 
 Functions carry the C names:
-  lora_workspace_size, lora_plan_build, lora_apply, lora_shrink, lora_expand,
+  lora_workspace_size, lora_plan_build, lora_apply, lora_apply_noalloc, lora_shrink, lora_expand,
   lora_apply_planned, lora_shrink_planned, lora_expand_planned,
   lora_apply_multi, lora_apply_sliced, lora_read_device_errors, lora_status_string.
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "lora_workspace_size": (SZ, [pb, I32]),
             "lora_plan_build": (ctypes.c_int, [pb, I32, P, SZ, P]),
             "lora_apply": (ctypes.c_int, [pp, pb, P, I64, P, I64, P, SZ, P]),
+            "lora_apply_noalloc": (ctypes.c_int, [pp, pb, P, I64, P, I64, P]),
             "lora_shrink": (ctypes.c_int, [pp, pb, P, I64, P, I64, P, SZ, P]),
             "lora_expand": (ctypes.c_int, [pp, pb, P, I64, P, I64, P, SZ, P]),
             "lora_apply_planned": (ctypes.c_int, [pp, pb, P, SZ, P, I64, P, I64, P]),
@@ -216,6 +217,14 @@ def lora_apply(pool: Pool, batch: Batch, x, y, ws):
     _check_rows("lora_apply", pool, batch, x=x, y=y, ws=ws)
     _check(lib().lora_apply(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(x), _ld(x), _ptr(y), _ld(y), _ptr(ws),
                             ws.numel(), _stream(y)), "lora_apply")
+
+
+def lora_apply_noalloc(pool: Pool, batch: Batch, x, y):
+    """lora_apply with the plan in the library's own device array (no workspace,
+    nothing allocated); calls that overlap on one GPU race."""
+    _check_rows("lora_apply_noalloc", pool, batch, x=x, y=y)
+    _check(lib().lora_apply_noalloc(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(x), _ld(x), _ptr(y), _ld(y),
+                                    _stream(y)), "lora_apply_noalloc")
 
 
 def lora_shrink(pool: Pool, batch: Batch, x, v, ws):

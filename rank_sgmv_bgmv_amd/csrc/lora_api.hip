@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "lora_internal.hpp"
 
@@ -284,11 +285,37 @@ lora_status run(int mode, const lora_pool *pool, const lora_batch *batch, const 
   return LORA_OK;
 }
 
+// Plan storage of lora_apply_noalloc: a fixed device array, one copy on every
+// GPU the library runs on, held until the process ends.  In host code the
+// array's name is only a host-side stand-in: kernels are given the device
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.
+constexpr size_t kNoAllocPlanBytes = size_t(8) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocPlanBytes];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device; nullptr if it cannot
+// be found.
+void *scratch_address() {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t lora_abi_version(void) { return 103; }
+int32_t lora_abi_version(void) { return 104; }
 
 const char *lora_status_string(lora_status s) {
   switch (s) {
@@ -323,6 +350,19 @@ lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *w
 lora_status lora_apply(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
                        int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
   return run(MODE_FUSED, pool, batch, ws, ws_bytes, true, x, ldx, y, ldy, nullptr, 0, stream);
+}
+
+lora_status lora_apply_noalloc(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
+                               int64_t ldy, hipStream_t stream) {
+  lora_status st = check_pool(pool);
+  if (st) return st;
+  BatchDims d;
+  if ((st = check_batch(batch, d))) return st;
+  if (pool->n_adapters < 1) return LORA_ESHAPE;
+  if (plan_layout(d.S, d.T, pool->n_adapters).total > kNoAllocPlanBytes) return LORA_EUNSUPPORTED;
+  void *plan = scratch_address();
+  if (!plan) return LORA_EHIP;
+  return run(MODE_FUSED, pool, batch, plan, kNoAllocPlanBytes, true, x, ldx, y, ldy, nullptr, 0, stream);
 }
 
 lora_status lora_shrink(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, float *v,

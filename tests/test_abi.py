@@ -40,7 +40,7 @@ def test_exported_symbols_match_binding(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lora_abi_version() == 103
+    assert lib.lora_abi_version() == 104
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.lora_status_string(st)
     assert b"workspace" in lib.lora_status_string(-3)
