@@ -60,6 +60,17 @@ __device__ __forceinline__ void gstore_at(T *base, uint32_t byte_off, const V &v
   *(LORA_GLOBAL R *)((LORA_GLOBAL char *)base + byte_off) = __builtin_bit_cast(R, v);
 }
 
+// A workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits until every global store the wave issued has completed; the kernels
+// here never read, within a launch, global memory another thread wrote, so
+// their barriers need not wait: a tile's y stores stay in flight while the
+// next tile or stage starts.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A value every lane of the wave holds (read from LDS tile metadata): moved to
 // a scalar register, so address arithmetic on it stays scalar and loads use a
 // scalar base plus a 32-bit lane offset.
@@ -232,7 +243,7 @@ __device__ __forceinline__ int adapter_rank(const ApplyArgs &a, int ad) {
 __device__ inline int setup_from_record(const ApplyArgs &a, int word, Meta &M) {
   const int tid = threadIdx.x;
   if (tid < kRecWords) M.rec[tid] = word;
-  __syncthreads();
+  lds_barrier();
   const int nrows = M.rec[R_NROWS], nact = M.rec[R_NACT];
   if (tid < nrows) {
     const int s = M.rec[R_S + tid];
@@ -250,7 +261,7 @@ __device__ inline int setup_from_record(const ApplyArgs &a, int word, Meta &M) {
     M.rk[tid] = adapter_rank(a, ad);
   }
   if (tid == 0) M.nact = nact;
-  __syncthreads();
+  lds_barrier();
   return nrows;
 }
 
@@ -290,18 +301,18 @@ __device__ inline void setup_rows(const ApplyArgs &a, int4 td, int n_active, Met
       ad[tid] = gload<int>(a.idx + e);
       sc[tid] = a.scale ? gload<float>(a.scale + e) : 1.0f;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < nrows) {
       M.t[tid] = td.w + tid;
       compact_slots(a, ad, sc, tid, M);
     }
-    __syncthreads();
+    lds_barrier();
     return;
   }
   // a tile's rows lie in requests q0 .. q0 + nrows - 1 (each holds >= 1 row)
   const int nq = min(nrows, n_active - q0);
   if (tid <= nq) M.cum[tid] = gload<int>(a.cumlen + q0 + tid);
-  __syncthreads();
+  lds_barrier();
   if (tid < nrows) {
     const int p = p0 + tid;
     int lo = 0, hi = min(tid, n_active - 1 - q0);
@@ -325,7 +336,7 @@ __device__ inline void setup_rows(const ApplyArgs &a, int4 td, int n_active, Met
     }
     if (tid == 0) M.nact = kk;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Zero the intermediate columns of the empty slots of every row of a tile
@@ -395,7 +406,7 @@ __device__ inline void walk_items(int64_t n_items, int per_unit, F &&body) {
     const int64_t item = unit * per_unit + k % per_unit;
     if (item >= n_items) break;
     body(item);
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
         dst[strip_row(c + 2 * i + 1) * AST] = uint16_t(wv[i] >> 16);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // --- walk the rows: lane (l16, kg) of wave w owns row o = row0 + 64 step + 16 w + l16
     //     and, in each 32-column group q, the columns 32 q + 8 kg .. +7.  The B

@@ -129,13 +129,13 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
     };
     // one stage: publish the A stage held in `ar`, prefetch the next, multiply
     auto step = [&](int kc, const uint4(&xc)[KS], uint4(&xn)[KS]) {
-      __syncthreads();  // every wave is done reading the previous stage
+      lds_barrier();  // every wave is done reading the previous stage
 #pragma unroll
       for (int i = 0; i < NAV; ++i) {
         const int e = tid + i * kThreads;
         *reinterpret_cast<uint4 *>(stage + (e / (KC / 8)) * AST + 8 * (e % (KC / 8))) = ar[i];
       }
-      __syncthreads();
+      lds_barrier();
       if (kc + KC < d_in) {
         load_a(kc + KC);
         load_x(kc + KC, xn);
@@ -210,7 +210,7 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int st = 0; st < n_st; ++st) {
     const int ob = o_lo + (st / nact) * NO, kk = st % nact;
-    __syncthreads();  // every wave is done reading the previous stage
+    lds_barrier();  // every wave is done reading the previous stage
     // block row o' = 32p + 8a + 4h + b goes to LDS row 32p + 16h + 4a + b:
     // output tile 2p + h then reads its rows 16(2p+h) .. +15 in order (no bank
     // conflicts), and its row 4a + b holds output 32p + 8a + 4h + b, so that
@@ -223,7 +223,7 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
       const int lrow = (row & ~31) | (((row >> 2) & 1) << 4) | (((row >> 3) & 3) << 2) | (row & 3);
       *reinterpret_cast<uint4 *>(stage + lrow * BST + 8 * (e % (R / 8))) = br[i];
     }
-    __syncthreads();
+    lds_barrier();
     if (st + 1 < n_st) {
       load_b(st + 1);
       if ((st + 1) % nact == 0) load_y(ob + NO, yn);

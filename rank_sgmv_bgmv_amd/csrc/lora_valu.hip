@@ -279,17 +279,20 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int row_lo
       }
     }
     if (MODE == MODE_SHRINK) continue;
-    __syncthreads();  // the intermediate of this row block is complete
+    lds_barrier();  // the intermediate of this row block is complete
     if (nb <= 1) valu_expand_rt<T, VEC, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
     else if (nb <= 2) valu_expand_rt<T, VEC, 2, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
     else valu_expand_rt<T, VEC, 4, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
-    __syncthreads();  // before the next row block overwrites the intermediate
+    lds_barrier();  // before the next row block overwrites the intermediate
   }
 }
 
 // ---------------------------------------------------------------- kernel --
-// At least four waves per SIMD (<= 128 VGPRs): the per-tile phases are short
-// dependent chains, and occupancy is what overlaps them.
+// Occupancy: the fused bf16 build takes about 250 VGPRs, so a SIMD holds two
+// waves and a CU two workgroups.  That is kept on purpose: holding the kernel
+// to 168 or 128 VGPRs (three or four waves) makes the compiler spill its
+// loads-in-flight and hoisted addresses to scratch, and the 32-layer decode
+// launch then runs 1.15x and 1.5x slower.
 template <typename T, bool VEC, int MODE>
 __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     }
     if (M.nact > 0 && row_lo < row_hi && (MODE == MODE_SHRINK || o_lo < o_hi))
       valu_tile<T, VEC, MODE>(a, cur.pr, row_lo, row_hi, o_lo, o_hi, c.d_out, M, s_v);
-    __syncthreads();
+    lds_barrier();
     it = nx;
     i += per_xcd;
     cur = nxt;
