@@ -50,7 +50,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 FLUSH_BYTES = 1 << 30
 
 # HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs
-# of `bench.py --only decode32` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# of `bench.py --only decode32` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch,
+# caches flushed before every step as in the timed runs),
 # each scaled by what the same counter reads for a plain copy of known size
 # (`bench.py --copy-calibration`: 256 MiB read + 256 MiB written per launch
 # reads FETCH_SIZE 131084 KiB and WRITE_SIZE 262144 KiB, so x2.0 and x1.0).
@@ -58,7 +59,7 @@ FLUSH_BYTES = 1 << 30
 # those sources change.
 TRAFFIC_SOURCES = ["rank_sgmv_bgmv_amd/csrc/lora_valu.hip", "rank_sgmv_bgmv_amd/csrc/lora_device.hpp",
                    "rank_sgmv_bgmv_amd/csrc/lora_internal.hpp"]
-MEASURED_TRAFFIC = {"sources_sha256_16": "f2b142c4cc45f5b0", "fetch_kib": 180004.5, "write_kib": 16384.0,
+MEASURED_TRAFFIC = {"sources_sha256_16": "05b24973a144f64a", "fetch_kib": 179594.2, "write_kib": 16384.0,
                     "fetch_scale": 2.0, "write_scale": 1.0}
 
 
