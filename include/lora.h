@@ -129,9 +129,12 @@ typedef struct {
 } lora_problem;
 
 /* Bytes of device workspace (the plan) for a batch and pool size.  The plan
- * holds the grouping of requests by adapter (stable across layers: build it
- * once per batch and reuse it for every adapted layer).  Returns 0 when the
- * batch description itself is invalid. */
+ * holds the grouping of requests by adapter -- the partition of the batch by
+ * LoRA index that "Serving several LoRAs, ControlNet and IP-Adapter",
+ * "Exercises" (the four-request answer), computes before one kernel covers
+ * every partition -- and it is stable across layers: build it once per batch
+ * and reuse it for every adapted layer.  Host only (nothing is launched);
+ * returns 0 when the batch description itself is invalid. */
 size_t lora_workspace_size(const lora_batch *batch, int32_t n_adapters);
 
 /* Build the plan for `batch` into `ws` on `stream`: sort requests by adapter
@@ -145,8 +148,12 @@ size_t lora_workspace_size(const lora_batch *batch, int32_t n_adapters);
 lora_status lora_plan_build(const lora_batch *batch, int32_t n_adapters, void *ws, size_t ws_bytes,
                             hipStream_t stream);
 
-/* Fused apply: y += sum_k scale * (x A_i^T) B_i^T for every touched row.
- * Builds the plan into ws, then runs the fused kernel.
+/* Fused apply ("Serving several LoRAs, ControlNet and IP-Adapter", section
+ * "LoRA: merged or alongside": the unmerged form adds x A^T B^T to the base
+ * output; "Exercises": rows grouped by adapter, one kernel for every group,
+ * results back in their rows; comparison table, stacking row: stacked LoRAs
+ * each add their own product): y += sum_k scale * (x A_i^T) B_i^T for every
+ * touched row.  Builds the plan into ws, then runs the fused kernels.
  *   x: [T][ldx] dtype, ldx >= d_in;  y: [T][ldy] dtype, ldy >= d_out.    */
 lora_status lora_apply(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
                        int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -169,21 +176,31 @@ lora_status lora_apply(const lora_pool *pool, const lora_batch *batch, const voi
 lora_status lora_apply_noalloc(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, void *y,
                                int64_t ldy, hipStream_t stream);
 
-/* Shrink half: v[t][k*rank + j] = scale[s][k] * sum_c x[t][c] A_i[j][c] for
+/* Shrink half ("Serving several LoRAs, ControlNet and IP-Adapter", section
+ * "LoRA: merged or alongside": the alongside form is two thin products, x A^T
+ * from d_in down to rank r, then that times B^T back up to d_out -- this is
+ * the first): v[t][k*rank + j] = scale[s][k] * sum_c x[t][c] A_i[j][c] for
  * every touched row t and slot k (zeros for a -1 slot of a touched row).
  * v: [T][ldv] float32, ldv >= max_slots*rank.  Rows that are not touched are
  * not written. */
 lora_status lora_shrink(const lora_pool *pool, const lora_batch *batch, const void *x, int64_t ldx, float *v,
                         int64_t ldv, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Expand half: y[t][o] += sum_{k valid} sum_j v[t][k*rank + j] B_i[o][j] for
- * every touched row (the scale is not applied again: lora_shrink folded it
- * in, so lora_expand(lora_shrink(x)) computes what lora_apply does). */
+/* Expand half (same section: the second thin product, rank r up to d_out,
+ * added to the base output): y[t][o] += sum_{k valid} sum_j v[t][k*rank + j]
+ * B_i[o][j] for every touched row (the scale is not applied again:
+ * lora_shrink folded it in, so lora_expand(lora_shrink(x)) computes what
+ * lora_apply does).  v is float32 [T][ldv], rows of untouched requests are
+ * not read. */
 lora_status lora_expand(const lora_pool *pool, const lora_batch *batch, const float *v, int64_t ldv, void *y,
                         int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The same three operations on a plan built earlier by lora_plan_build for
- * this batch (plan_bytes as returned by lora_workspace_size). */
+ * this batch (plan_bytes as returned by lora_workspace_size): the grouping of
+ * the "Exercises" answer done once per batch and reused by every adapted
+ * layer.  A plan built for another batch shape or pool size is detected on
+ * the device: the kernels then write nothing and count the call in the
+ * plan's error word (lora_read_device_errors). */
 lora_status lora_apply_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
                                const void *x, int64_t ldx, void *y, int64_t ldy, hipStream_t stream);
 lora_status lora_shrink_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
@@ -191,9 +208,14 @@ lora_status lora_shrink_planned(const lora_pool *pool, const lora_batch *batch, 
 lora_status lora_expand_planned(const lora_pool *pool, const lora_batch *batch, const void *plan, size_t plan_bytes,
                                 const float *v, int64_t ldv, void *y, int64_t ldy, hipStream_t stream);
 
-/* Many adapted layers of one shape in ONE launch, sharing one plan: for each
- * of the n_problems entries of `problems` (a DEVICE array), the fused apply
- * with that problem's pool, x and y.  `shape` gives rank, d_in, d_out,
+/* Many adapted layers of one shape in ONE launch, sharing one plan ("Serving
+ * several LoRAs, ControlNet and IP-Adapter", section "LoRA: merged or
+ * alongside": every adapted linear layer of the model -- its cost table
+ * counts the attention projections of all 57 layers -- gets its own
+ * alongside product for the same requests; "Exercises": one kernel for every
+ * group).  For each of the n_problems entries of `problems` (a DEVICE array,
+ * read by the kernels, so that a launch needs no host copy of it), the fused
+ * apply with that problem's pool, x and y.  `shape` gives rank, d_in, d_out,
  * n_adapters, dtype and ranks (its A and B are ignored; its rank array, if
  * any, applies to every problem).  The library cannot check
  * the pointers inside the device array; they must satisfy the alignment and
@@ -264,8 +286,10 @@ typedef struct {
   int64_t ldw;
 } lora_merge_problem;
 
-/* lora_merge for n_problems weights of one shape in ONE launch: for each
- * entry of `problems` (a DEVICE array), W += alpha * sum_k scale[k] B_i A_i
+/* lora_merge for n_problems weights of one shape in ONE launch (same section:
+ * merging touches every affected weight of the model, the page's cost model
+ * counts all of them): for each entry of `problems` (a DEVICE array),
+ * W += alpha * sum_k scale[k] B_i A_i
  * with i = idx[k] taken from that entry's pool.  `shape` gives rank, d_in,
  * d_out, n_adapters, dtype and ranks (its A and B are ignored; its rank
  * array, if any, applies to every problem); idx and scale are
@@ -295,14 +319,21 @@ lora_status lora_merge_multi(const lora_pool *shape, const int32_t *idx, const f
 lora_status lora_pool_load(const lora_pool *pool, int32_t slot, const void *A_host, const void *B_host,
                            hipStream_t stream);
 
-/* Synchronizes `stream` and stores in *count the number of invalid adapter
- * indices and segment-offset violations the last plan build met. */
+/* Not an operation of the method: the pages define no error reporting.  It
+ * reads what the device could not check on the host -- the adapter indices
+ * below -1 or >= n_adapters that the last plan build skipped, the segment
+ * offsets it clamped, and one for every apply launch that found the plan not
+ * matching its call (another batch shape or pool size, or no plan at all) and
+ * did nothing.  Synchronizes `stream` (the only call that does) and stores the
+ * count in *count (a HOST pointer); the return value is the call's own status
+ * (LORA_EINVAL for NULL arguments, LORA_EWORKSPACE for a plan_bytes too small
+ * to hold the header, LORA_EHIP if the copy or the synchronization fails). */
 lora_status lora_read_device_errors(const void *plan, size_t plan_bytes, int32_t *count, hipStream_t stream);
 
-/* Static, human-readable text for a status. */
+/* Static, human-readable text for a status (not an operation of the method). */
 const char *lora_status_string(lora_status status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor; not an operation of the method). */
 int32_t lora_abi_version(void);
 
 #ifdef __cplusplus

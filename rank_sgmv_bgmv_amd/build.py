@@ -1,9 +1,15 @@
 """Build the HIP library (gfx950) in-tree: rank_sgmv_bgmv_amd/_build/liblora_hip.so.
 
-    python -m rank_sgmv_bgmv_amd.build [--verbose]
+    python -m rank_sgmv_bgmv_amd.build [--verbose] [--asan]
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled.  The result is a plain C-ABI shared library (include/lora.h).
+
+--asan builds _build/liblora_hip_asan.so instead: the host code (argument
+checks, workspace layout, launch configuration) instrumented with
+AddressSanitizer, the device code as usual.  It is for CPU-side tests of the
+C ABI's validation path: load it into a process started with the sanitizer
+runtime preloaded (asan_runtime() gives its path).
 """
 from __future__ import annotations
 
@@ -36,8 +42,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra=()) -> str:
+ASAN_LIB = os.path.join(OUT_DIR, "liblora_hip_asan.so")
+# host-only sanitizer flags: every -fsanitize applies to the host pass alone
+ASAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the AddressSanitizer runtime of the compiler hipcc drives."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    res = subprocess.run([clang, "--print-resource-dir"], capture_output=True, text=True, check=True).stdout.strip()
+    return os.path.join(res, "lib", "linux", "libclang_rt.asan-x86_64.so")
+
+
+def build(verbose: bool = False, extra=(), asan: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
+    lib_path = ASAN_LIB if asan else LIB
+    if asan:
+        extra = [*extra, *ASAN_FLAGS]
     objs = []
     with tempfile.TemporaryDirectory(dir=OUT_DIR) as tmp:
         procs = []
@@ -50,20 +73,20 @@ def build(verbose: bool = False, extra=()) -> str:
             objs.append(obj)
         failed = []
         for src, p in procs:
-            out, _ = p.communicate()
-            if out and (verbose or p.returncode):
-                print(out, file=sys.stderr)
+            log, _ = p.communicate()
+            if log and (verbose or p.returncode):
+                print(log, file=sys.stderr)
             if p.returncode:
                 failed.append(src)
         if failed:
             raise RuntimeError(f"hipcc failed for {failed}")
-        tmp_lib = LIB + f".tmp{os.getpid()}"
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        tmp_lib = lib_path + f".tmp{os.getpid()}"
+        link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-libsan"] if asan else []
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp_lib]
         subprocess.run(cmd, check=True)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    build(verbose="--verbose" in sys.argv)
-    print(LIB)
+    print(build(verbose="--verbose" in sys.argv, asan="--asan" in sys.argv))
