@@ -19,6 +19,7 @@ struct Tune {
   int mfma_items = 256;   // aim for about this many MFMA work items per launch
   int grid_cap = 2048;    // workgroups per launch; the kernels grid-stride over items
   int mfma_half = -1;     // MFMA half-size stages: -1 when they let two workgroups share a CU, 0 never, 1 always
+  int mfma_stacked = 1;   // fused launches with 2 .. 4 slots per request: x walked once per stacked tile (0: per slot)
 };
 
 int env_int(const char *name, int dflt) {
@@ -35,6 +36,7 @@ const Tune &tune() {
     x.mfma_items = env_int("LORA_MFMA_ITEMS", x.mfma_items);
     x.grid_cap = env_int("LORA_GRID_CAP", x.grid_cap);
     x.mfma_half = env_int("LORA_MFMA_HALF", x.mfma_half);
+    x.mfma_stacked = env_int("LORA_MFMA_STACKED", x.mfma_stacked);
     return x;
   }();
   return t;
@@ -126,6 +128,7 @@ struct Launch {
   bool vec;
   int jt;           // rank / 16 when the MFMA kernel runs, else 0
   bool half;        // MFMA kernel with half-size stages
+  int smax;         // MFMA kernel's stacked-tile build (2 or 4 slots), or 1
   int grid_v, grid_m;
   size_t smem_v, smem_m;
 };
@@ -189,6 +192,13 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     L.half = true;
     L.smem_m = mfma_smem_bytes(L.jt, d.K, true);
   }
+  // requests that stack 2 .. 4 adapters: their tiles walk x once for all slots
+  L.smax = 1;
+  if (mfma && tn.mfma_stacked && mode == MODE_FUSED && d.K >= 2 && d.K <= 4) {
+    L.smax = d.K == 2 ? 2 : 4;
+    L.half = false;
+    L.smem_m = mfma_stacked_smem_bytes(L.jt, L.smax);
+  }
   // what the MFMA kernel needs to choose between the plan's two tilings
   a.n_cu = cu_count();
   const int per_cu = L.smem_m ? (int)std::min<size_t>(2, std::max<size_t>(1, kMaxLdsBytes / L.smem_m)) : 2;
@@ -199,7 +209,8 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
 // MFMA tiles (the long groups) first, then the VALU tiles.
 hipError_t launch_all(int mode, int dtype, const Launch &L, const ApplyArgs &a, hipStream_t stream) {
   if (L.jt > 0) {
-    hipError_t e = launch_mfma(mode, L.jt, L.half, a, L.grid_m, L.smem_m, stream);
+    hipError_t e = L.smax > 1 ? launch_mfma_stacked(L.jt, L.smax, a, L.grid_m, L.smem_m, stream)
+                              : launch_mfma(mode, L.jt, L.half, a, L.grid_m, L.smem_m, stream);
     if (e != hipSuccess) return e;
   }
   return launch_valu(mode, dtype, L.vec, a, L.grid_v, L.smem_v, stream);

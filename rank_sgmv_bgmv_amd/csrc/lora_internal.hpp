@@ -204,5 +204,9 @@ hipError_t launch_valu(int mode, int dtype, bool vec, const ApplyArgs &args, int
 // MFMA kernel (bf16, vector path): jt = rank / 16 in {1, 2, 4, 8}.
 hipError_t launch_mfma(int mode, int jt, bool half, const ApplyArgs &args, int grid, size_t smem,
                        hipStream_t stream);
+// MFMA kernel for fused launches whose requests stack 2 .. smax (2 or 4) slots:
+// a tile with several slots walks x once for all of them.
+size_t mfma_stacked_smem_bytes(int jt, int smax);
+hipError_t launch_mfma_stacked(int jt, int smax, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
 
 }  // namespace lora

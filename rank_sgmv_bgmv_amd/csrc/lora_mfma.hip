@@ -33,6 +33,14 @@
 // A second build halves both stages (d_in columns per shrink stage, outputs
 // per expand stage) for tiles with many stacked slots, whose parked
 // intermediates would otherwise leave LDS for one workgroup per CU.
+//
+// Stacked slots (comparison table, stacking row: every stacked LoRA adds its
+// own alongside product to the same x).  In a launch whose requests stack
+// two to four adapters, a tile with several slots walks x once for all of
+// them: each x stage is multiplied by every slot's staged A into that slot's
+// accumulators, and the slots' bf16 intermediates stay in registers through
+// the expand (instead of parking in LDS), so all slots' A stages fit beside
+// each other.  Single-slot tiles of the same launch take the path above.
 
 #include "lora_device.hpp"
 
@@ -264,9 +272,216 @@ __device__ void mfma_tile(const ApplyArgs &a, const lora_problem &pr, int nrows,
   }
 }
 
+// ---------------------------------------------------------- stacked tiles --
+// A stages of SMAX slots side by side in LDS: d_in columns per stage chosen so
+// that they hold about 16 K elements together (32 KB), which keeps the next
+// stage's A (prefetched into registers) at 32 registers a lane.
+template <int JT, int SMAX>
+struct StackCfg {
+  static constexpr int R = 16 * JT;
+  static constexpr int KC0 = 16384 / (SMAX * R);
+  static constexpr int KC = KC0 >= 256 ? 256 : KC0 >= 128 ? 128 : KC0 >= 64 ? 64 : 32;  // d_in columns per stage
+  static constexpr int KS = KC / 32;                       // k-steps per stage
+  static constexpr int AST = KC + 8;                       // staged A row stride (elements)
+  static constexpr int NAV = R * (KC / 8) / kThreads;      // 16-byte A pieces per thread per stage and slot
+  static constexpr int SST = R * AST;                      // elements between two slots' A stages
+  static constexpr int NO = 128;                           // outputs per expand stage
+  static constexpr int OT = NO / 16;
+  static constexpr int BST = R + 8;
+  static constexpr int NBV = NO * (R / 8) / kThreads;
+  static constexpr size_t LDS = (size_t(SMAX) * SST > size_t(NO) * BST ? size_t(SMAX) * SST : size_t(NO) * BST) * 2;
+  static_assert(NAV >= 1 && NBV >= 1, "stage sizes");
+};
+
+// A tile whose rows carry 2 .. SMAX slots (fused mode): one walk over d_in,
+// the slots' intermediates in registers, then the expand of every output
+// block over every slot.
+template <int JT, int SMAX>
+__device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi,
+                                  int d_out, const Meta &M, uint16_t *stage) {
+  typedef StackCfg<JT, SMAX> C;
+  constexpr int R = C::R, KC = C::KC, KS = C::KS, AST = C::AST, NAV = C::NAV, SST = C::SST;
+  constexpr int NO = C::NO, OT = C::OT, BST = C::BST, NBV = C::NBV;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int m = 16 * w + l16;  // this lane's tile row
+  const bool row_ok = m < nrows;
+  const bool wave_live = 16 * w < nrows;
+  const int d_in = a.d_in, nact = uniform(M.nact);
+  const int64_t trow = M.t[row_ok ? m : 0];
+  const uint16_t *__restrict__ xrow = static_cast<const uint16_t *>(pr.x) + trow * pr.ldx;
+  uint16_t *__restrict__ yrow = static_cast<uint16_t *>(pr.y) + trow * pr.ldy;
+
+  // ------------------------------------------------------------ shrink --
+  f32x4 acc[SMAX][JT];
+#pragma unroll
+  for (int g = 0; g < SMAX; ++g)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[g][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 ar[SMAX][NAV];    // next A stage of every slot (cooperative)
+  uint4 x0[KS], x1[KS];   // x operands of the current / next stage (this lane's row)
+  auto load_a = [&](int kc) {
+#pragma unroll
+    for (int g = 0; g < SMAX; ++g) {
+      const int gg = min(g, nact - 1);
+      const uint16_t *__restrict__ Ag = static_cast<const uint16_t *>(pr.A) + (int64_t)M.a[gg] * R * d_in;
+      const int rk = g < nact ? M.rk[gg] : 0;  // rows past the adapter's rank (or an unused slot) are zeros
+#pragma unroll
+      for (int i = 0; i < NAV; ++i) {
+        const int e = tid + i * kThreads;
+        const int row = e / (KC / 8), c = kc + 8 * (e % (KC / 8));
+        ar[g][i] = (c < d_in && row < rk) ? gload<uint4>(Ag + (int64_t)row * d_in + c) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto load_x = [&](int kc, uint4(&xr)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = kc + 32 * ks + 8 * kg;
+      xr[ks] = (row_ok && c < d_in) ? gload<uint4>(xrow + c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto step = [&](int kc, const uint4(&xc)[KS], uint4(&xn)[KS]) {
+    lds_barrier();  // every wave is done reading the previous stage
+#pragma unroll
+    for (int g = 0; g < SMAX; ++g) {
+      if (g < nact) {
+#pragma unroll
+        for (int i = 0; i < NAV; ++i) {
+          const int e = tid + i * kThreads;
+          *reinterpret_cast<uint4 *>(stage + g * SST + (e / (KC / 8)) * AST + 8 * (e % (KC / 8))) = ar[g][i];
+        }
+      }
+    }
+    lds_barrier();
+    if (kc + KC < d_in) {
+      load_a(kc + KC);
+      load_x(kc + KC, xn);
+    }
+    if (wave_live) {
+#pragma unroll
+      for (int g = 0; g < SMAX; ++g) {
+        if (g < nact) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+              const uint4 av =
+                  *reinterpret_cast<const uint4 *>(stage + g * SST + (16 * jt + l16) * AST + 32 * ks + 8 * kg);
+              acc[g][jt] = mfma32(av, xc[ks], acc[g][jt]);
+            }
+          }
+        }
+      }
+    }
+  };
+  load_a(0);
+  load_x(0, x0);
+  for (int kc = 0; kc < d_in; kc += 2 * KC) {
+    step(kc, x0, x1);
+    if (kc + KC < d_in) step(kc + KC, x1, x0);
+  }
+  // acc[g][jt][q] = v_g[t_m][16 jt + 4 kg + q]: scaled and rounded once to bf16
+  // it is the B operand of the expand's MFMA for this lane's row
+  uint2 v[SMAX][JT];
+#pragma unroll
+  for (int g = 0; g < SMAX; ++g) {
+    const float sc = (row_ok && g < nact) ? M.sc[m][min(g, nact - 1)] : 0.f;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const f32x4 sv = acc[g][jt] * sc;
+      v[g][jt] = make_uint2(pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3]));
+    }
+  }
+
+  // ------------------------------------------------------------ expand --
+  // stages are (output block, slot), slot-minor, as in mfma_tile
+  const int n_ob = (o_hi - o_lo + NO - 1) / NO;
+  const int n_st = n_ob * nact;
+  uint4 br[NBV];
+  uint4 yc[OT / 2], yn[OT / 2];
+  f32x4 yacc[OT];
+  auto load_b = [&](int st) {
+    const int ob = o_lo + (st / nact) * NO, kk = st % nact;
+    const uint16_t *__restrict__ Bk = static_cast<const uint16_t *>(pr.B) + (int64_t)M.a[kk] * d_out * R;
+    const int rk = M.rk[kk];
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / (R / 8), c = 8 * (e % (R / 8));
+      br[i] = (ob + row < o_hi && c < rk) ? gload<uint4>(Bk + (int64_t)(ob + row) * R + c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto load_y = [&](int ob, uint4(&yr)[OT / 2]) {
+#pragma unroll
+    for (int p = 0; p < OT / 2; ++p) {
+      const int o = ob + 32 * p + 8 * kg;
+      yr[p] = (row_ok && o < o_hi) ? gload<uint4>(yrow + o) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (n_st > 0) {
+    load_b(0);
+    load_y(o_lo, yc);
+  }
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < n_st; ++st) {
+    const int ob = o_lo + (st / nact) * NO, kk = st % nact;
+    lds_barrier();  // every wave is done reading the previous stage
+    // the interleaved row order of mfma_tile's expand stages (two 16-wide
+    // output tiles give each lane 8 consecutive outputs of its row)
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) {
+      const int e = tid + i * kThreads;
+      const int row = e / (R / 8);
+      const int lrow = (row & ~31) | (((row >> 2) & 1) << 4) | (((row >> 3) & 3) << 2) | (row & 3);
+      *reinterpret_cast<uint4 *>(stage + lrow * BST + 8 * (e % (R / 8))) = br[i];
+    }
+    lds_barrier();
+    if (st + 1 < n_st) {
+      load_b(st + 1);
+      if ((st + 1) % nact == 0) load_y(ob + NO, yn);
+    }
+    if (wave_live) {
+#pragma unroll
+      for (int g = 0; g < SMAX; ++g) {
+        if (g == kk) {
+#pragma unroll
+          for (int ot = 0; ot < OT; ++ot) {
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+              const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
+              yacc[ot] = mfma16(bv, v[g][jt], yacc[ot]);
+            }
+          }
+        }
+      }
+    }
+    if (kk == nact - 1) {
+#pragma unroll
+      for (int p = 0; p < OT / 2; ++p) {
+        const int o = ob + 32 * p + 8 * kg;
+        if (row_ok && o < o_hi) {
+          const uint4 y0 = yc[p];
+          const f32x4 lo = yacc[2 * p], hi = yacc[2 * p + 1];
+          gstore(yrow + o, make_uint4(pack_bf2(bf_lo(y0.x) + lo[0], bf_hi(y0.x) + lo[1]),
+                                      pack_bf2(bf_lo(y0.y) + lo[2], bf_hi(y0.y) + lo[3]),
+                                      pack_bf2(bf_lo(y0.z) + hi[0], bf_hi(y0.z) + hi[1]),
+                                      pack_bf2(bf_lo(y0.w) + hi[2], bf_hi(y0.w) + hi[3])));
+        }
+        yc[p] = yn[p];
+      }
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
 // ---------------------------------------------------------------- kernel --
-template <int JT, int HS, int MODE>
-__global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
+// SMAX > 1 (fused launches whose requests stack 2 .. SMAX adapters): tiles
+// with several slots take mfma_tile_stacked, the others mfma_tile.
+template <int JT, int HS, int MODE, int SMAX>
+__device__ __forceinline__ void mfma_kernel_body(ApplyArgs &a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Meta &M = *reinterpret_cast<Meta *>(smem);
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
@@ -296,9 +511,29 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
     const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + c.slice) : a.single;
     const int4 td = gload<int4>(tiles + tile);
     setup_rows(a, td, n_active, M);
-    if (M.nact > 0 && (MODE == MODE_SHRINK || c.o_lo < c.o_hi))
+    if (M.nact > 0 && (MODE == MODE_SHRINK || c.o_lo < c.o_hi)) {
+      if constexpr (SMAX > 1) {
+        if (M.nact > 1) {
+          mfma_tile_stacked<JT, SMAX>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage);
+          return;
+        }
+      }
       mfma_tile<JT, HS, MODE>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage, vpark);
+    }
   });
+}
+
+template <int JT, int HS, int MODE>
+__global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
+  mfma_kernel_body<JT, HS, MODE, 1>(a);
+}
+
+// The stacked-slot build, held to two waves per SIMD (two workgroups per CU):
+// left to itself the compiler would give the wide stacks more registers and
+// halve the occupancy.
+template <int JT, int SMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void mfma_stacked_kernel(ApplyArgs a) {
+  mfma_kernel_body<JT, 1, MODE_FUSED, SMAX>(a);
 }
 
 // Launch one instantiation; the first launch lifts its dynamic-LDS limit to
@@ -310,6 +545,16 @@ hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t str
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
   hipLaunchKernelGGL((mfma_kernel<JT, HS, M>), dim3(grid), dim3(kThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int JT, int SMAX>
+hipError_t launch_stacked(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  static const bool lds_limit_raised =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_stacked_kernel<JT, SMAX>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+  (void)lds_limit_raised;
+  hipLaunchKernelGGL((mfma_stacked_kernel<JT, SMAX>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -343,6 +588,42 @@ size_t mfma_smem_bytes(int jt, int slots, bool half) {
 
 // Half stages are built for ranks 64 and 128 only: smaller ranks park little.
 bool mfma_half_available(int jt) { return jt == 4 || jt == 8; }
+
+// The stacked-slot build: meta + the larger of the stacked A stages and the
+// single-slot path's staging with one parked intermediate.
+template <int JT, int SMAX>
+size_t stacked_smem_of() {
+  const size_t single = MfmaCfg<JT, 1>::LDS + size_t(kMfmaRows) * MfmaCfg<JT, 1>::VST * 2;
+  return kMetaBytes + (StackCfg<JT, SMAX>::LDS > single ? StackCfg<JT, SMAX>::LDS : single);
+}
+
+size_t mfma_stacked_smem_bytes(int jt, int smax) {
+  switch (jt * 16 + smax) {
+    case 16 + 2: return stacked_smem_of<1, 2>();
+    case 16 + 4: return stacked_smem_of<1, 4>();
+    case 32 + 2: return stacked_smem_of<2, 2>();
+    case 32 + 4: return stacked_smem_of<2, 4>();
+    case 64 + 2: return stacked_smem_of<4, 2>();
+    case 64 + 4: return stacked_smem_of<4, 4>();
+    case 128 + 2: return stacked_smem_of<8, 2>();
+    case 128 + 4: return stacked_smem_of<8, 4>();
+  }
+  return 0;
+}
+
+hipError_t launch_mfma_stacked(int jt, int smax, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  switch (jt * 16 + smax) {
+    case 16 + 2: return launch_stacked<1, 2>(a, grid, smem, stream);
+    case 16 + 4: return launch_stacked<1, 4>(a, grid, smem, stream);
+    case 32 + 2: return launch_stacked<2, 2>(a, grid, smem, stream);
+    case 32 + 4: return launch_stacked<2, 4>(a, grid, smem, stream);
+    case 64 + 2: return launch_stacked<4, 2>(a, grid, smem, stream);
+    case 64 + 4: return launch_stacked<4, 4>(a, grid, smem, stream);
+    case 128 + 2: return launch_stacked<8, 2>(a, grid, smem, stream);
+    case 128 + 4: return launch_stacked<8, 4>(a, grid, smem, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_mfma(int mode, int jt, bool half, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   switch (jt) {
