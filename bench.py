@@ -709,7 +709,12 @@ def main():
         log("c3 ...")
         variants["C3_prefill_r64"] = bench_single(W.case_c3(), dev, K, Wm, flusher, "C3 prefill r64")
     if want("c5"):
-        for d, r in [(1280, 64), (1280, 128), (640, 64), (640, 128)]:
+        # LORA_BENCH_C5="1280x64,640x128" narrows the sweep (a profiled run per shape)
+        c5 = [(1280, 64), (1280, 128), (640, 64), (640, 128)]
+        pick = os.environ.get("LORA_BENCH_C5", "")
+        if pick:
+            c5 = [tuple(int(v) for v in s.split("x")) for s in pick.split(",")]
+        for d, r in c5:
             log(f"c5 d{d} r{r} ...")
             variants[f"C5_d{d}_r{r}"] = bench_single(W.case_c5(d, r), dev, K, Wm, flusher, f"C5 diffusion d{d} r{r}")
     if want("stacked"):

@@ -11,6 +11,7 @@
 namespace lora {
 
 constexpr int kPlanThreads = 1024;  // one workgroup builds the plan
+constexpr int kPlanSmallThreads = 256;  // the plan of a batch of at most 64 requests
 constexpr int kThreads = 256;       // apply kernels: 4 wave64s per workgroup
 constexpr int kValuThreads = 256;   // VALU kernel workgroup
 constexpr int kMfmaRows = 64;       // rows per MFMA tile (16 per wave)

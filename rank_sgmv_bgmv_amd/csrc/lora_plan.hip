@@ -334,16 +334,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
   }
 }
 
-// Batches of at most 64 requests: one wave, one request per lane, no
-// workgroup barriers beyond the wave's own.  The counting sort becomes a rank
-// by comparison -- stable, by key and then by request, so the order inside a
-// group is fixed -- and every scan a wave scan.  Same plan as plan_kernel.
-__global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *__restrict__ seg_off,
-                                                        const int *__restrict__ idx) {
+// Batches of at most 64 requests: one request per lane of a wave.  The
+// counting sort becomes a rank by comparison -- stable, by key and then by
+// request, so the order inside a group is fixed -- and every scan a wave scan.
+// Same plan as plan_kernel.  Every wave of the workgroup computes the same
+// sort and scans from the same inputs (so each holds the tile counts in its
+// registers) and wave 0 alone writes the shared arrays; the tile descriptors,
+// one binary search over the groups and one over the requests each, are then
+// shared out over all kPlanSmallThreads threads (a long prefill batch has
+// thousands of tiles).
+__global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView P, const int *__restrict__ seg_off,
+                                                                       const int *__restrict__ idx) {
   __shared__ int s_sseg[64], s_sst[64], s_key[64], s_cum[65], s_gstart[65], s_toff_m[65], s_toff_v[65], s_toff_ms[65];
   __shared__ int s_idx[64 * LORA_MAX_SLOTS];  // the batch's idx [S][K], read once from memory
   __shared__ __align__(16) int s_keyin[64];    // every request's key, for the rank
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool w0 = tid < 64;  // the wave that writes the shared arrays
   const int S = P.S, T = P.T, n = P.n, K = P.K;
   const bool req = lane < S;
   int err = 0;
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
     for (int k = 0; k < LORA_MAX_SLOTS; ++k) {
       if (k < K) {
         const int a = ads[k];
-        s_idx[lane * K + k] = a;
+        if (w0) s_idx[lane * K + k] = a;
         if (a != -1) {
           if (a < -1 || a >= n) {
             ++err;
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   // 3. stable rank among the active requests: every key is read back from LDS
   // in 16-byte pieces, all in flight at once (a cross-lane read per key would
   // wait for each in turn)
-  s_keyin[lane] = key;
+  if (w0) s_keyin[lane] = key;
   __syncthreads();
   int rank = 0;
 #pragma unroll
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   }
   const unsigned long long act = __ballot(key >= 0);
   const int n_active = __popcll(act);
-  if (key >= 0) {
+  if (w0 && key >= 0) {
     s_sseg[rank] = lane;
     s_sst[rank] = st;
     s_key[rank] = key;
@@ -416,10 +422,10 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   const int ginc = wave_incl_scan_add(flag);
   const int n_groups = __shfl(ginc, 63);
   __syncthreads();
-  if (live) s_cum[lane] = inc - len;
-  if (lane == 0) s_cum[n_active] = total_rows;
-  if (flag) s_gstart[ginc - 1] = lane;
-  if (lane == 0) s_gstart[n_groups] = n_active;
+  if (w0 && live) s_cum[lane] = inc - len;
+  if (tid == 0) s_cum[n_active] = total_rows;
+  if (w0 && flag) s_gstart[ginc - 1] = lane;
+  if (tid == 0) s_gstart[n_groups] = n_active;
   __syncthreads();
   // 5. tiles per group (lane g)
   int nm = 0, nv = 0, nms = 0;
@@ -432,31 +438,31 @@ __global__ __launch_bounds__(64) void plan_kernel_small(PlanView P, const int *_
   }
   const int im = wave_incl_scan_add(nm), iv = wave_incl_scan_add(nv), ims = wave_incl_scan_add(nms);
   const int nt_m = __shfl(im, 63), nt_v = __shfl(iv, 63), nt_ms = __shfl(ims, 63);
-  if (lane < n_groups) {
+  if (w0 && lane < n_groups) {
     s_toff_m[lane] = im - nm;
     s_toff_v[lane] = iv - nv;
     s_toff_ms[lane] = ims - nms;
   }
-  if (lane == 0) {
+  if (tid == 0) {
     s_toff_m[n_groups] = nt_m;
     s_toff_v[n_groups] = nt_v;
     s_toff_ms[n_groups] = nt_ms;
   }
   __syncthreads();
   // 6. tile descriptors and records
-  for (int u = lane; u < nt_m + nt_v; u += 64)
+  for (int u = tid; u < nt_m + nt_v; u += kPlanSmallThreads)
     emit_tile(P, s_idx, u, nt_m, n_groups, s_toff_m, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
-  for (int u = lane; u < nt_ms; u += 64)
+  for (int u = tid; u < nt_ms; u += kPlanSmallThreads)
     P.tiles_ms[u] = mfma_tile_desc(s_toff_ms, kMfmaRowsSmall, u, n_groups, s_gstart, s_cum, s_sseg, s_sst);
   // the apply kernels read these three arrays for MFMA tiles
-  if (live) {
+  if (w0 && live) {
     P.sseg[lane] = s_sseg[lane];
     P.sst[lane] = s_sst[lane];
     P.cumlen[lane] = s_cum[lane];
   }
-  if (lane == 0) P.cumlen[n_active] = total_rows;
+  if (tid == 0) P.cumlen[n_active] = total_rows;
   for (int o = 32; o > 0; o >>= 1) err += __shfl_xor(err, o);
-  if (lane == 0) {
+  if (tid == 0) {
     P.hdr[H_TILES_MS] = nt_ms;
     P.hdr[H_TILES_M] = nt_m;
     P.hdr[H_TILES_V] = nt_v;
@@ -480,7 +486,7 @@ hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, 
                           int(kPlanLdsBudget)) == hipSuccess;
   (void)lds_limit_raised;
   if (P.S <= 64)
-    hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(64), 0, stream, P, seg_off, idx);
+    hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(kPlanSmallThreads), 0, stream, P, seg_off, idx);
   else
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), P.lds_mode ? lds_bytes : 0, stream, P, seg_off, idx);
   return hipGetLastError();
