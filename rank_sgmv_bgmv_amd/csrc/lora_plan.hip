@@ -122,9 +122,6 @@ __device__ __forceinline__ int last_le(const int *a, int lo, int hi, int key) {
   return lo;
 }
 
-// Tile u (MFMA tiles first, then VALU tiles): its descriptor {first sorted
-// row, first request, rows, group end}, and for a VALU tile its record (rows,
-// requests, compacted slots: all rows of a tile share their adapters).
 // Descriptor of tile uu of an MFMA tiling of `rows_per` rows per tile (toff:
 // the tiling's first tile of each group).  A tile inside one request carries
 // that request and its first token row ({p0, request, rows, first token row});
@@ -141,28 +138,22 @@ __device__ int4 mfma_tile_desc(const int *toff, int rows_per, int uu, int n_grou
   return single ? make_int4(p0, sseg[q0], nrows, sst[q0] + (p0 - cumlen[q0])) : make_int4(p0, q0, nrows, -1);
 }
 
-__device__ void emit_tile(const PlanView &P, const int *__restrict__ idx, int u, int nt_m, int n_groups,
-                          const int *toff_m, const int *toff_v, const int *gstart, const int *cumlen, const int *sseg,
-                          const int *sst) {
-  if (u < nt_m) {
-    P.tiles_m[u] = mfma_tile_desc(toff_m, kMfmaRows, u, n_groups, gstart, cumlen, sseg, sst);
-    return;
-  }
-  const int uu = u - nt_m;
+// Row i of VALU tile uu (the tile's descriptor {first sorted row, first
+// request, rows, group end} and record: rows, requests, compacted slots -- all
+// rows of a tile share their adapters).  One thread per row: the row-0 thread
+// also writes the descriptor, the row count and the slots; every thread writes
+// its row's token, request and slot positions (zeros past the tile's rows).
+__device__ void emit_vrow(const PlanView &P, const int *__restrict__ idx, int uu, int i, int n_groups,
+                          const int *toff_v, const int *gstart, const int *cumlen, const int *sseg, const int *sst) {
   const int g = last_le(toff_v, 0, n_groups - 1, uu);
   const int gs = gstart[g], ge = gstart[g + 1];
   const int p0 = cumlen[gs] + (uu - toff_v[g]) * kValuRows;
   const int nrows = min(kValuRows, cumlen[ge] - p0);
-  const int q0 = last_le(cumlen, gs, ge - 1, p0);
-  const int4 d = make_int4(p0, q0, nrows, ge);
-  P.tiles_v[uu] = d;
   int *R = P.vrec + (int64_t)uu * kRecWords;
-  int q = q0, nact = 0;
-  for (int w = 0; w < kValuRows * LORA_MAX_SLOTS / 4; ++w) R[R_POS + w] = 0;
-  uint8_t *pos = reinterpret_cast<uint8_t *>(R + R_POS);
-  for (int i = 0; i < nrows; ++i) {
+  uint32_t pw[2] = {0u, 0u};  // pos[i][0 .. 7], one byte per compacted slot
+  if (i < nrows) {
     const int p = p0 + i;
-    while (cumlen[q + 1] <= p) ++q;
+    const int q = last_le(cumlen, gs, ge - 1, p);
     const int s = sseg[q];
     R[R_T + i] = sst[q] + (p - cumlen[q]);
     R[R_S + i] = s;
@@ -171,13 +162,17 @@ __device__ void emit_tile(const PlanView &P, const int *__restrict__ idx, int u,
       const int ad = idx[(int64_t)s * P.K + k];
       if (ad < 0 || ad >= P.n) continue;
       if (i == 0) R[R_A + kk] = ad;
-      pos[i * LORA_MAX_SLOTS + kk] = uint8_t(k);
+      pw[kk >> 2] |= uint32_t(k) << (8 * (kk & 3));
       ++kk;
     }
-    if (i == 0) nact = kk;
+    if (i == 0) {
+      R[R_NROWS] = nrows;
+      R[R_NACT] = kk;
+      P.tiles_v[uu] = make_int4(p0, q, nrows, ge);
+    }
   }
-  R[R_NROWS] = nrows;
-  R[R_NACT] = nact;
+  R[R_POS + 2 * i] = int(pw[0]);
+  R[R_POS + 2 * i + 1] = int(pw[1]);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const int *__restrict__ seg_off,
@@ -302,8 +297,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanView P, const in
   __syncthreads();
 
   // 6. tile descriptors; VALU tiles also get a record; then the second MFMA tiling
-  for (int u = tid; u < nt_m + nt_v; u += kPlanThreads)
-    emit_tile(P, idx, u, nt_m, n_groups, toff_m, toff_v, gstart, cumlen, sseg, sst);
+  for (int u = tid; u < nt_m; u += kPlanThreads)
+    P.tiles_m[u] = mfma_tile_desc(toff_m, kMfmaRows, u, n_groups, gstart, cumlen, sseg, sst);
+  for (int w = tid; w < nt_v * kValuRows; w += kPlanThreads)
+    emit_vrow(P, idx, w / kValuRows, w % kValuRows, n_groups, toff_v, gstart, cumlen, sseg, sst);
   for (int u = tid; u < nt_ms; u += kPlanThreads)
     P.tiles_ms[u] = mfma_tile_desc(toff_ms, kMfmaRowsSmall, u, n_groups, gstart, cumlen, sseg, sst);
 
@@ -347,7 +344,7 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
                                                                        const int *__restrict__ idx) {
   __shared__ int s_sseg[64], s_sst[64], s_key[64], s_cum[65], s_gstart[65], s_toff_m[65], s_toff_v[65], s_toff_ms[65];
   __shared__ int s_idx[64 * LORA_MAX_SLOTS];  // the batch's idx [S][K], read once from memory
-  __shared__ __align__(16) int s_keyin[64];    // every request's key, for the rank
+  __shared__ __align__(16) long long s_ck[64];  // every request's (key, request) pair, for the rank
   const int tid = threadIdx.x, lane = tid & 63;
   const bool w0 = tid < 64;  // the wave that writes the shared arrays
   const int S = P.S, T = P.T, n = P.n, K = P.K;
@@ -388,20 +385,21 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
     }
     key = (en - st <= 0 || nact == 0) ? -1 : (nact == 1 ? a0 : n);
   }
-  // 3. stable rank among the active requests: every key is read back from LDS
-  // in 16-byte pieces, all in flight at once (a cross-lane read per key would
-  // wait for each in turn)
-  if (w0) s_keyin[lane] = key;
+  // 3. stable rank among the active requests: (key, request) as one 64-bit
+  // value, the inactive requests after every active one, so the rank is a
+  // count of smaller values -- one compare and one add per request, on values
+  // read back from LDS in 16-byte pieces, all in flight at once
+  const long long ck = key >= 0 ? (static_cast<long long>(key) << 6) | lane : LLONG_MAX;
+  if (w0) s_ck[lane] = ck;
   __syncthreads();
   int rank = 0;
 #pragma unroll
-  for (int j4 = 0; j4 < 16; ++j4) {
-    const int4 q = reinterpret_cast<const int4 *>(s_keyin)[j4];
-    const int j = 4 * j4;
-    rank += q.x >= 0 && (q.x < key || (q.x == key && j < lane));
-    rank += q.y >= 0 && (q.y < key || (q.y == key && j + 1 < lane));
-    rank += q.z >= 0 && (q.z < key || (q.z == key && j + 2 < lane));
-    rank += q.w >= 0 && (q.w < key || (q.w == key && j + 3 < lane));
+  for (int h = 0; h < 4; ++h) {
+    longlong2 q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = reinterpret_cast<const longlong2 *>(s_ck)[8 * h + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rank += int(q[j].x < ck) + int(q[j].y < ck);
   }
   const unsigned long long act = __ballot(key >= 0);
   const int n_active = __popcll(act);
@@ -450,8 +448,10 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
   }
   __syncthreads();
   // 6. tile descriptors and records
-  for (int u = tid; u < nt_m + nt_v; u += kPlanSmallThreads)
-    emit_tile(P, s_idx, u, nt_m, n_groups, s_toff_m, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
+  for (int u = tid; u < nt_m; u += kPlanSmallThreads)
+    P.tiles_m[u] = mfma_tile_desc(s_toff_m, kMfmaRows, u, n_groups, s_gstart, s_cum, s_sseg, s_sst);
+  for (int w = tid; w < nt_v * kValuRows; w += kPlanSmallThreads)
+    emit_vrow(P, s_idx, w / kValuRows, w % kValuRows, n_groups, s_toff_v, s_gstart, s_cum, s_sseg, s_sst);
   for (int u = tid; u < nt_ms; u += kPlanSmallThreads)
     P.tiles_ms[u] = mfma_tile_desc(s_toff_ms, kMfmaRowsSmall, u, n_groups, s_gstart, s_cum, s_sseg, s_sst);
   // the apply kernels read these three arrays for MFMA tiles
