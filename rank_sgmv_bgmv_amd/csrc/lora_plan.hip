@@ -40,25 +40,33 @@
 namespace lora {
 namespace {
 
+// Inclusive prefix sum / maximum over the 64 lanes of a wave, in registers
+// (no LDS round trips): DPP row shifts by 1, 2, 4 and 8 lanes scan each row of
+// 16 lanes, then the last lane of rows 0 and 2 is folded into rows 1 and 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).  A lane with no
+// source lane takes the identity.  Every lane of the wave must be active.
 __device__ __forceinline__ int wave_incl_scan_add(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
 __device__ __forceinline__ int wave_incl_scan_max(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(v, o);
-    if (lane >= o) v = max(v, u);
-  }
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xc, 0xf, false));
   return v;
 }
+
+// The value lane 63 of the wave holds (a scalar read, no LDS round trip).
+__device__ __forceinline__ int wave_last(int v) { return __builtin_amdgcn_readlane(v, 63); }
 
 // Exclusive prefix sum of one value per thread over the 1024-thread block.
 __device__ int block_excl_scan_add(int v, int *sh, int &total) {
@@ -350,21 +358,37 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
   const int S = P.S, T = P.T, n = P.n, K = P.K;
   const bool req = lane < S;
   int err = 0;
+  // every load of the batch at once -- both offsets and every slot's index --
+  // through clamped addresses (lanes past the batch read its last request and
+  // drop the values), so the plan waits for one round trip to memory
+  int v0 = INT_MIN, v1 = INT_MIN;
+  int ads[LORA_MAX_SLOTS];
+#pragma unroll
+  for (int k = 0; k < LORA_MAX_SLOTS; ++k) ads[k] = -1;
+  if (S > 0) {
+    const int ls = min(lane, S - 1);
+    if (!P.per_token) {
+      v0 = seg_off[ls];
+      v1 = seg_off[ls + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < LORA_MAX_SLOTS; ++k) ads[k] = idx[(int64_t)ls * K + min(k, K - 1)];
+  }
+  if (!req) {
+    v0 = v1 = INT_MIN;
+#pragma unroll
+    for (int k = 0; k < LORA_MAX_SLOTS; ++k) ads[k] = -1;
+  }
   // 1. sanitised request bounds [st, en): the prefix maximum of the offsets, clamped to [0, T]
   int st = lane, en = lane + 1;
   if (!P.per_token) {
-    const int v0 = req ? seg_off[lane] : INT_MIN, v1 = req ? seg_off[lane + 1] : INT_MIN;
     if (req) err += (lane == 0 && v0 < 0) + (v1 < v0) + (lane == S - 1 && v1 > T);
     const int m = wave_incl_scan_max(v0);
     st = min(max(m, 0), T);
     en = min(max(max(m, v1), 0), T);
   }
   // 2. key: the only valid adapter, n for several (each such request is its own group), -1 for none
-  // (every slot's index in flight at once, clamped addresses; kept in LDS for
-  // the tile records)
-  int ads[LORA_MAX_SLOTS];
-#pragma unroll
-  for (int k = 0; k < LORA_MAX_SLOTS; ++k) ads[k] = req ? idx[(int64_t)lane * K + min(k, K - 1)] : -1;
+  // (the indices are kept in LDS for the tile records)
   int key = -1;
   if (req) {
     int nact = 0, a0 = -1;
@@ -414,11 +438,11 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
   const bool live = lane < n_active;
   const int len = live ? s_cum[lane] : 0, kq = live ? s_key[lane] : -1;
   const int inc = wave_incl_scan_add(len);
-  const int total_rows = __shfl(inc, 63);
+  const int total_rows = wave_last(inc);
   const int kprev = __shfl_up(kq, 1);
   const int flag = live && (lane == 0 || kq == n || kq != kprev) ? 1 : 0;
   const int ginc = wave_incl_scan_add(flag);
-  const int n_groups = __shfl(ginc, 63);
+  const int n_groups = wave_last(ginc);
   __syncthreads();
   if (w0 && live) s_cum[lane] = inc - len;
   if (tid == 0) s_cum[n_active] = total_rows;
@@ -435,7 +459,7 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
     nms = big ? (rows + kMfmaRowsSmall - 1) / kMfmaRowsSmall : 0;
   }
   const int im = wave_incl_scan_add(nm), iv = wave_incl_scan_add(nv), ims = wave_incl_scan_add(nms);
-  const int nt_m = __shfl(im, 63), nt_v = __shfl(iv, 63), nt_ms = __shfl(ims, 63);
+  const int nt_m = wave_last(im), nt_v = wave_last(iv), nt_ms = wave_last(ims);
   if (w0 && lane < n_groups) {
     s_toff_m[lane] = im - nm;
     s_toff_v[lane] = iv - nv;
@@ -461,7 +485,7 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
     P.cumlen[lane] = s_cum[lane];
   }
   if (tid == 0) P.cumlen[n_active] = total_rows;
-  for (int o = 32; o > 0; o >>= 1) err += __shfl_xor(err, o);
+  err = wave_last(wave_incl_scan_add(err));
   if (tid == 0) {
     P.hdr[H_TILES_MS] = nt_ms;
     P.hdr[H_TILES_M] = nt_m;
