@@ -30,7 +30,9 @@
  * and owned by the caller; the library allocates and frees nothing and is
  * re-entrant.  The only state it keeps between calls is looked up once and
  * never changes: each device's compute-unit count, the kernels' LDS limit,
- * and the tuning values read from the environment at the first call.  Every
+ * the tuning values read from the environment at the first call, and each
+ * device's address of the fixed plan array that lora_apply_noalloc uses (a
+ * static device array of the library, not an allocation).  Every
  * compute call is asynchronous on the given stream and never synchronizes,
  * except lora_read_device_errors.
  * x and y must not overlap; v must overlap neither x nor y.
