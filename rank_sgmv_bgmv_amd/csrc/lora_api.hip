@@ -173,6 +173,8 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     a.cvo[p + 1] = a.cvo[p] + a.cv[p];
     a.cmo[p + 1] = a.cmo[p] + a.cm[p];
   }
+  a.items_v_tile = a.cvo[ns];
+  a.items_m_tile = a.cmo[ns];
 
   const int64_t items_m = (int64_t)n_groups * std::max(P.L.bound_m, P.L.bound_ms) * a.cmo[ns];
   // the VALU kernel takes an MFMA-sized tile as one item per row block
@@ -193,8 +195,9 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     L.smem_m = mfma_smem_bytes(L.jt, d.K, true);
   }
   // requests that stack 2 .. 4 adapters: their tiles walk x once for all slots
+  // (single-slice launches; a sliced launch keeps one pass per slot)
   L.smax = 1;
-  if (mfma && tn.mfma_stacked && mode == MODE_FUSED && d.K >= 2 && d.K <= 4) {
+  if (mfma && tn.mfma_stacked && mode == MODE_FUSED && ns == 1 && d.K >= 2 && d.K <= 4) {
     L.smax = d.K == 2 ? 2 : 4;
     L.half = false;
     L.smem_m = mfma_stacked_smem_bytes(L.jt, L.smax);

@@ -360,20 +360,25 @@ struct Chunk {
 };
 // The slice tables are read at constant indices only (an unrolled scan): an
 // index known only at run time into the kernel's argument block makes the
-// compiler copy the array to scratch memory.
+// compiler copy the array to scratch memory.  NSL: the slices the build
+// handles (1 for every launch but lora_apply_sliced's, which then keeps no
+// scan in registers).  IS_M: 1 for the MFMA tiling's chunks, 0 for the VALU
+// tiling's, -1 when only `is_m` knows.
+template <int NSL = LORA_MAX_SLICES, int IS_M = -1>
 __device__ inline Chunk chunk_of(const ApplyArgs &a, bool is_m, int q) {
+  const bool m = IS_M < 0 ? is_m : IS_M == 1;
   Chunk c;
   c.slice = 0;
   c.d_out = a.sd_out[0];
-  int base = 0, width = is_m ? a.wm[0] : a.wv[0];
+  int base = 0, width = m ? a.wm[0] : a.wv[0];
 #pragma unroll
-  for (int p = 1; p < LORA_MAX_SLICES; ++p) {
-    const int off = is_m ? a.cmo[p] : a.cvo[p];
+  for (int p = 1; p < NSL; ++p) {
+    const int off = m ? a.cmo[p] : a.cvo[p];
     if (p < a.ns && q >= off) {  // chunk offsets increase with p: the last match is q's slice
       c.slice = p;
       c.d_out = a.sd_out[p];
       base = off;
-      width = is_m ? a.wm[p] : a.wv[p];
+      width = m ? a.wm[p] : a.wv[p];
     }
   }
   c.o_lo = (q - base) * width;

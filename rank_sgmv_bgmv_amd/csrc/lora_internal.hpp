@@ -165,6 +165,10 @@ struct ApplyArgs {
   int sd_out[LORA_MAX_SLICES];
   int cv[LORA_MAX_SLICES], wv[LORA_MAX_SLICES], cm[LORA_MAX_SLICES], wm[LORA_MAX_SLICES];
   int cvo[LORA_MAX_SLICES + 1], cmo[LORA_MAX_SLICES + 1];
+  // cvo[ns] and cmo[ns] (a tile's VALU and MFMA items over every slice), as
+  // plain fields: an index known only at run time into the tables above would
+  // make the kernels copy them to scratch memory
+  int items_v_tile, items_m_tile;
   // split API: float32 intermediate [T][ldv]
   float *v;
   int64_t ldv;

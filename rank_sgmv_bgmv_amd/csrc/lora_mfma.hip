@@ -479,9 +479,11 @@ __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, in
 
 // ---------------------------------------------------------------- kernel --
 // SMAX > 1 (fused launches whose requests stack 2 .. SMAX adapters): tiles
-// with several slots take mfma_tile_stacked, the others mfma_tile.
-template <int JT, int HS, int MODE, int SMAX>
-__device__ __forceinline__ void mfma_kernel_body(ApplyArgs &a) {
+// with several slots take mfma_tile_stacked, the others mfma_tile.  NSL: the
+// output slices the build handles (LORA_MAX_SLICES for lora_apply_sliced's
+// launches, 1 for all others).
+template <int JT, int HS, int MODE, int SMAX, int NSL>
+__device__ __forceinline__ void mfma_kernel_body(const ApplyArgs &a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Meta &M = *reinterpret_cast<Meta *>(smem);
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
@@ -489,7 +491,7 @@ __device__ __forceinline__ void mfma_kernel_body(ApplyArgs &a) {
   const PlanHdr ph = read_plan_header(a);
   if (!ph.ok) return;
   const int n_m64 = ph.n_m, n_ms = ph.n_ms, n_active = ph.n_active;
-  const int per_tile = a.cmo[a.ns];  // items of one tile, over every slice
+  const int per_tile = NSL == 1 ? a.items_m_tile : a.cmo[a.ns];  // items of one tile, over every slice
   // The plan's 48-row tiling when the 64-row items are more than the CUs (so
   // some CUs would run two and set the launch's duration) but the 48-row items
   // all fit on the chip at once: the CUs that run two then hold 96 rows
@@ -507,7 +509,7 @@ __device__ __forceinline__ void mfma_kernel_body(ApplyArgs &a) {
     // adapters (the longest tiles: a shrink and an expand pass per slot)
     // last, and they should start first rather than form the launch's tail
     const int tile = n_m - 1 - int(rem / per_tile);
-    const Chunk c = chunk_of(a, true, int(rem % per_tile));
+    const Chunk c = chunk_of<NSL, 1>(a, true, int(rem % per_tile));
     const lora_problem pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + c.slice) : a.single;
     const int4 td = gload<int4>(tiles + tile);
     setup_rows(a, td, n_active, M);
@@ -523,28 +525,28 @@ __device__ __forceinline__ void mfma_kernel_body(ApplyArgs &a) {
   });
 }
 
-template <int JT, int HS, int MODE>
+template <int JT, int HS, int MODE, int NSL>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(ApplyArgs a) {
-  mfma_kernel_body<JT, HS, MODE, 1>(a);
+  mfma_kernel_body<JT, HS, MODE, 1, NSL>(a);
 }
 
 // The stacked-slot build, held to two waves per SIMD (two workgroups per CU):
 // left to itself the compiler would give the wide stacks more registers and
-// halve the occupancy.
+// halve the occupancy.  Launched for single-slice calls only.
 template <int JT, int SMAX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void mfma_stacked_kernel(ApplyArgs a) {
-  mfma_kernel_body<JT, 1, MODE_FUSED, SMAX>(a);
+  mfma_kernel_body<JT, 1, MODE_FUSED, SMAX, 1>(a);
 }
 
 // Launch one instantiation; the first launch lifts its dynamic-LDS limit to
 // the 160 KB a gfx950 workgroup may use.
-template <int JT, int HS, int M>
+template <int JT, int HS, int M, int NSL>
 hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_kernel<JT, HS, M>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_kernel<JT, HS, M, NSL>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
-  hipLaunchKernelGGL((mfma_kernel<JT, HS, M>), dim3(grid), dim3(kThreads), smem, stream, a);
+  hipLaunchKernelGGL((mfma_kernel<JT, HS, M, NSL>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -558,12 +560,16 @@ hipError_t launch_stacked(const ApplyArgs &a, int grid, size_t smem, hipStream_t
   return hipGetLastError();
 }
 
+// Launches with several output slices are fused ones (lora_apply_sliced).
 template <int JT, int HS>
 hipError_t launch_jt(int mode, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  if (a.ns > 1)
+    return mode == MODE_FUSED ? launch_one<JT, HS, MODE_FUSED, LORA_MAX_SLICES>(a, grid, smem, stream)
+                              : hipErrorInvalidValue;
   switch (mode) {
-    case MODE_FUSED: return launch_one<JT, HS, MODE_FUSED>(a, grid, smem, stream);
-    case MODE_SHRINK: return launch_one<JT, HS, MODE_SHRINK>(a, grid, smem, stream);
-    case MODE_EXPAND: return launch_one<JT, HS, MODE_EXPAND>(a, grid, smem, stream);
+    case MODE_FUSED: return launch_one<JT, HS, MODE_FUSED, 1>(a, grid, smem, stream);
+    case MODE_SHRINK: return launch_one<JT, HS, MODE_SHRINK, 1>(a, grid, smem, stream);
+    case MODE_EXPAND: return launch_one<JT, HS, MODE_EXPAND, 1>(a, grid, smem, stream);
   }
   return hipErrorInvalidValue;
 }

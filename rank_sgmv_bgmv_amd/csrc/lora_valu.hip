@@ -293,7 +293,9 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int row_lo
 // to 168 or 128 VGPRs (three or four waves) makes the compiler spill its
 // loads-in-flight and hoisted addresses to scratch, and the 32-layer decode
 // launch then runs 1.15x and 1.5x slower.
-template <typename T, bool VEC, int MODE>
+// NSL: the output slices the build handles (LORA_MAX_SLICES for
+// lora_apply_sliced's launches, 1 for all others).
+template <typename T, bool VEC, int MODE, int NSL>
 __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   Meta &M = *reinterpret_cast<Meta *>(smem);
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
   // take a 64-row tile's row blocks one after another).  A tile's items run
   // over every slice of the group (per_v / per_m of them per row block).
   constexpr int kSubBlocks = kMfmaRows / kRowBlock;
-  const int per_v = a.cvo[a.ns], per_m = a.cmo[a.ns] * kSubBlocks;
+  const int per_v = a.items_v_tile, per_m = a.items_m_tile * kSubBlocks;
   const int64_t items_v = (int64_t)n_v * per_v;
   const int64_t items_m = a.valu_takes_m ? (int64_t)n_m * per_m : 0;
   const int64_t per_grp = items_v + items_m;
@@ -343,10 +345,10 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     h.tile = (h.is_m ? n_m : n_v) - 1 - h.tile;
     h.sb = 0;
     if (h.is_m) {  // an MFMA-sized tile: row block, then slice and chunk
-      h.sb = h.q / a.cmo[a.ns];
-      h.q -= h.sb * a.cmo[a.ns];
+      h.sb = h.q / a.items_m_tile;
+      h.q -= h.sb * a.items_m_tile;
     }
-    const int slice = chunk_of(a, h.is_m, h.q).slice;
+    const int slice = chunk_of<NSL>(a, h.is_m, h.q).slice;
     h.pr = a.probs ? gload<lora_problem>(a.probs + (int64_t)g * a.ns + slice) : a.single;
     h.word = 0;
     if (!h.is_m && threadIdx.x < kRecWords) h.word = gload<int>(a.vrec + (int64_t)h.tile * kRecWords + threadIdx.x);
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
     Ahead nxt;
     nxt.word = 0;
     if (nx >= 0) load_ahead(nx, nxt);
-    const Chunk c = chunk_of(a, cur.is_m, cur.q);
+    const Chunk c = chunk_of<NSL>(a, cur.is_m, cur.q);
     const int o_lo = c.o_lo, o_hi = c.o_hi;
     int row_lo = 0, row_hi;
     if (cur.is_m) {
@@ -383,22 +385,26 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
 
 // Launch one instantiation; the first launch lifts its dynamic-LDS limit to
 // the 160 KB a gfx950 workgroup may use.
-template <typename T, bool VEC, int M>
+template <typename T, bool VEC, int M, int NSL>
 hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&valu_kernel<T, VEC, M>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&valu_kernel<T, VEC, M, NSL>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
-  hipLaunchKernelGGL((valu_kernel<T, VEC, M>), dim3(grid), dim3(kValuThreads), smem, stream, a);
+  hipLaunchKernelGGL((valu_kernel<T, VEC, M, NSL>), dim3(grid), dim3(kValuThreads), smem, stream, a);
   return hipGetLastError();
 }
 
+// Launches with several output slices are fused ones (lora_apply_sliced).
 template <typename T, bool VEC>
 hipError_t launch_mode(int mode, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  if (a.ns > 1)
+    return mode == MODE_FUSED ? launch_one<T, VEC, MODE_FUSED, LORA_MAX_SLICES>(a, grid, smem, stream)
+                              : hipErrorInvalidValue;
   switch (mode) {
-    case MODE_FUSED: return launch_one<T, VEC, MODE_FUSED>(a, grid, smem, stream);
-    case MODE_SHRINK: return launch_one<T, VEC, MODE_SHRINK>(a, grid, smem, stream);
-    case MODE_EXPAND: return launch_one<T, VEC, MODE_EXPAND>(a, grid, smem, stream);
+    case MODE_FUSED: return launch_one<T, VEC, MODE_FUSED, 1>(a, grid, smem, stream);
+    case MODE_SHRINK: return launch_one<T, VEC, MODE_SHRINK, 1>(a, grid, smem, stream);
+    case MODE_EXPAND: return launch_one<T, VEC, MODE_EXPAND, 1>(a, grid, smem, stream);
   }
   return hipErrorInvalidValue;
 }
