@@ -20,6 +20,7 @@ struct Tune {
   int grid_cap = 2048;    // workgroups per launch; the kernels grid-stride over items
   int mfma_half = -1;     // MFMA half-size stages: -1 when they let two workgroups share a CU, 0 never, 1 always
   int mfma_stacked = 1;   // fused launches with 2 .. 4 slots per request: x walked once per stacked tile (0: per slot)
+  int mfma_contig = 1;    // MFMA tiles of equal cost dealt to the XCDs in contiguous ranges (0: blocks round-robin)
 };
 
 int env_int(const char *name, int dflt) {
@@ -37,6 +38,7 @@ const Tune &tune() {
     x.grid_cap = env_int("LORA_GRID_CAP", x.grid_cap);
     x.mfma_half = env_int("LORA_MFMA_HALF", x.mfma_half);
     x.mfma_stacked = env_int("LORA_MFMA_STACKED", x.mfma_stacked);
+    x.mfma_contig = env_int("LORA_MFMA_CONTIG", x.mfma_contig);
     return x;
   }();
   return t;
@@ -202,6 +204,12 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     L.half = false;
     L.smem_m = mfma_stacked_smem_bytes(L.jt, L.smax);
   }
+  // One slot per request and one rank: every MFMA tile costs about the same,
+  // and a launch over many problems deals each XCD whole problems, whose
+  // adapters then sit in that XCD's L2 only.  (A single problem keeps the
+  // round-robin blocks: C3 fetched 16% less with contiguous ranges but ran
+  // 1.4% slower, its tiles being bound by one round trip per stage.)
+  a.mfma_uniform = tn.mfma_contig && n_groups > 1 && d.K == 1 && shape->ranks == nullptr ? 1 : 0;
   // what the MFMA kernel needs to choose between the plan's two tilings
   a.n_cu = cu_count();
   const int per_cu = L.smem_m ? (int)std::min<size_t>(2, std::max<size_t>(1, kMaxLdsBytes / L.smem_m)) : 2;

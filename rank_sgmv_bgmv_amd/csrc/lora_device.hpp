@@ -399,12 +399,16 @@ __device__ inline Chunk chunk_of(const ApplyArgs &a, bool is_m, int q) {
 // consecutive tiles, because those mostly share an adapter, which an XCD then
 // stages into its L2 once per block rather than once per tile; whole units, so
 // that the slices and chunks of a tile share one L2 (and its x).
+// With `contiguous` (every unit costs about the same) each XCD takes one
+// contiguous eighth of the units instead, so the tiles that share an adapter
+// stay on one or two XCDs and the adapter is staged into that many L2s.
 constexpr int kUnitBlock = 8;
 template <class F>
-__device__ inline void walk_items(int64_t n_items, int per_unit, F &&body) {
+__device__ inline void walk_items(int64_t n_items, int per_unit, F &&body, bool contiguous = false) {
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
   const int64_t n_units = (n_items + per_unit - 1) / per_unit;
-  const int blk = (int)min<int64_t>(kUnitBlock, max<int64_t>(1, n_units / 64));
+  const int64_t blk = contiguous ? max<int64_t>(1, (n_units + 7) / 8)
+                                 : min<int64_t>(kUnitBlock, max<int64_t>(1, n_units / 64));
   for (int64_t k = lb;; k += per_xcd) {
     const int64_t u = k / per_unit;  // the XCD's u-th unit
     const int64_t unit = (xcd + 8 * (u / blk)) * blk + u % blk;

@@ -169,6 +169,9 @@ struct ApplyArgs {
   // plain fields: an index known only at run time into the tables above would
   // make the kernels copy them to scratch memory
   int items_v_tile, items_m_tile;
+  // every MFMA tile costs about the same (one slot per request, one rank):
+  // the MFMA kernel deals contiguous ranges of tiles to the XCDs
+  int mfma_uniform;
   // split API: float32 intermediate [T][ldv]
   float *v;
   int64_t ldv;

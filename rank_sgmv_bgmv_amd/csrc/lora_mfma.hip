@@ -522,7 +522,7 @@ __device__ __forceinline__ void mfma_kernel_body(const ApplyArgs &a) {
       }
       mfma_tile<JT, HS, MODE>(a, pr, td.z, c.o_lo, c.o_hi, c.d_out, M, stage, vpark);
     }
-  });
+  }, a.mfma_uniform != 0);
 }
 
 template <int JT, int HS, int MODE, int NSL>

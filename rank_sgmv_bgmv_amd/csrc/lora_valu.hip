@@ -288,11 +288,11 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int row_lo
 }
 
 // ---------------------------------------------------------------- kernel --
-// Occupancy: the fused bf16 build takes about 250 VGPRs, so a SIMD holds two
-// waves and a CU two workgroups.  That is kept on purpose: holding the kernel
-// to 168 or 128 VGPRs (three or four waves) makes the compiler spill its
-// loads-in-flight and hoisted addresses to scratch, and the 32-layer decode
-// launch then runs 1.15x and 1.5x slower.
+// Occupancy: the fused bf16 single-slice build takes about 200 VGPRs, so a
+// SIMD holds two waves and a CU two workgroups.  That is kept on purpose:
+// holding the kernel to 168 VGPRs (three waves) makes the compiler spill its
+// loads in flight and hoisted addresses to scratch, and the 32-layer decode
+// launch then runs about 10% slower (1.5x at 128 VGPRs, four waves).
 // NSL: the output slices the build handles (LORA_MAX_SLICES for
 // lora_apply_sliced's launches, 1 for all others).
 template <typename T, bool VEC, int MODE, int NSL>
