@@ -200,7 +200,7 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   // (single-slice launches; a sliced launch keeps one pass per slot)
   L.smax = 1;
   if (mfma && tn.mfma_stacked && mode == MODE_FUSED && ns == 1 && d.K >= 2 && d.K <= 4) {
-    L.smax = d.K == 2 ? 2 : 4;
+    L.smax = d.K;  // builds for 2, 3 and 4 slots
     L.half = false;
     L.smem_m = mfma_stacked_smem_bytes(L.jt, L.smax);
   }

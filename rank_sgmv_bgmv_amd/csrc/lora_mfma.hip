@@ -606,12 +606,16 @@ size_t stacked_smem_of() {
 size_t mfma_stacked_smem_bytes(int jt, int smax) {
   switch (jt * 16 + smax) {
     case 16 + 2: return stacked_smem_of<1, 2>();
+    case 16 + 3: return stacked_smem_of<1, 3>();
     case 16 + 4: return stacked_smem_of<1, 4>();
     case 32 + 2: return stacked_smem_of<2, 2>();
+    case 32 + 3: return stacked_smem_of<2, 3>();
     case 32 + 4: return stacked_smem_of<2, 4>();
     case 64 + 2: return stacked_smem_of<4, 2>();
+    case 64 + 3: return stacked_smem_of<4, 3>();
     case 64 + 4: return stacked_smem_of<4, 4>();
     case 128 + 2: return stacked_smem_of<8, 2>();
+    case 128 + 3: return stacked_smem_of<8, 3>();
     case 128 + 4: return stacked_smem_of<8, 4>();
   }
   return 0;
@@ -620,12 +624,16 @@ size_t mfma_stacked_smem_bytes(int jt, int smax) {
 hipError_t launch_mfma_stacked(int jt, int smax, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   switch (jt * 16 + smax) {
     case 16 + 2: return launch_stacked<1, 2>(a, grid, smem, stream);
+    case 16 + 3: return launch_stacked<1, 3>(a, grid, smem, stream);
     case 16 + 4: return launch_stacked<1, 4>(a, grid, smem, stream);
     case 32 + 2: return launch_stacked<2, 2>(a, grid, smem, stream);
+    case 32 + 3: return launch_stacked<2, 3>(a, grid, smem, stream);
     case 32 + 4: return launch_stacked<2, 4>(a, grid, smem, stream);
     case 64 + 2: return launch_stacked<4, 2>(a, grid, smem, stream);
+    case 64 + 3: return launch_stacked<4, 3>(a, grid, smem, stream);
     case 64 + 4: return launch_stacked<4, 4>(a, grid, smem, stream);
     case 128 + 2: return launch_stacked<8, 2>(a, grid, smem, stream);
+    case 128 + 3: return launch_stacked<8, 3>(a, grid, smem, stream);
     case 128 + 4: return launch_stacked<8, 4>(a, grid, smem, stream);
   }
   return hipErrorInvalidValue;
