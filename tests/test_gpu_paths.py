@@ -7,7 +7,8 @@
   * the plan kernel with its working arrays in global memory (batches whose
     arrays exceed its LDS budget) and with scans over more than one 1024-wide
     chunk;
-  * rank 1 and eight stacked slots on the apply path;
+  * rank 1 and eight stacked slots on the apply path; every build of the
+    stacked MFMA kernel (2, 3 and 4 slots at ranks 16 to 128);
   * a plan that does not match the call: no work, counted in the error word.
 
 "Serving several LoRAs, ControlNet and IP-Adapter", "Exercises" (four
@@ -49,6 +50,7 @@ GRID_CAP_SUBSET = [
     "test_gpu_merge.py::test_merge_grid",
     "test_gpu_merge.py::test_merge_multi_equals_single_calls",
     "test_gpu_ranks.py::test_ranks_parity",
+    "test_gpu_paths.py::test_stacked_builds",
 ]
 
 
@@ -122,6 +124,20 @@ def test_rank_one(orc, dtype, vec):
 def test_eight_slots(orc, name, kw):
     """Eight stacked slots per request (the largest slot count), some empty."""
     case = W.random_case(7300 + len(name), K=8, with_scale=True, p_empty=0.25, **kw)
+    _full_case(orc, case)
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+def test_stacked_builds(orc, r, K):
+    """Every build of the stacked MFMA kernel (ranks 16-128, 2, 3 and 4 slots
+    per request): requests with 1 .. K valid slots in one launch, d_in not a
+    multiple of any stage width, per-slot scales.  "Serving several LoRAs,
+    ControlNet and IP-Adapter", comparison table, stacking row: each stacked
+    LoRA adds its own product to the output."""
+    case = W.random_case(7500 + 10 * r + K, dtype=W.BF16, n=9, r=r, d_in=328, d_out=200, S=6, K=K,
+                         min_len=30, max_len=90, with_scale=True, p_empty=0.2)
+    assert case.batch.T >= 128  # the MFMA path
     _full_case(orc, case)
 
 
