@@ -21,6 +21,7 @@ struct Tune {
   int mfma_half = -1;     // MFMA half-size stages: -1 when they let two workgroups share a CU, 0 never, 1 always
   int mfma_stacked = 1;   // fused launches with 2 .. 4 slots per request: x walked once per stacked tile (0: per slot)
   int mfma_contig = 1;    // MFMA tiles of equal cost dealt to the XCDs in contiguous ranges (0: blocks round-robin)
+  int mfma_xonce = 1;     // sliced launches (2 .. 4 slices, one slot per request): x walked once per tile (0: per slice)
 };
 
 int env_int(const char *name, int dflt) {
@@ -39,6 +40,7 @@ const Tune &tune() {
     x.mfma_half = env_int("LORA_MFMA_HALF", x.mfma_half);
     x.mfma_stacked = env_int("LORA_MFMA_STACKED", x.mfma_stacked);
     x.mfma_contig = env_int("LORA_MFMA_CONTIG", x.mfma_contig);
+    x.mfma_xonce = env_int("LORA_MFMA_XONCE", x.mfma_xonce);
     return x;
   }();
   return t;
@@ -130,7 +132,8 @@ struct Launch {
   bool vec;
   int jt;           // rank / 16 when the MFMA kernel runs, else 0
   bool half;        // MFMA kernel with half-size stages
-  int smax;         // MFMA kernel's stacked-tile build (2 or 4 slots), or 1
+  int smax;         // MFMA kernel's stacked-tile build (2, 3 or 4 slots), or 1
+  int nsl;          // MFMA kernel walking x once for the nsl slices of a group (sliced launches), or 0
   int grid_v, grid_m;
   size_t smem_v, smem_m;
 };
@@ -204,6 +207,22 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
     L.half = false;
     L.smem_m = mfma_stacked_smem_bytes(L.jt, L.smax);
   }
+  // Sliced launches with one slot per request: one item per row tile for all
+  // 2 .. 4 slices of a group, which walks x once for every slice (the tile
+  // then covers each slice's whole width: no output chunks).  Taken when the
+  // slices' outputs are narrow next to x (q / k / v: the same time as one item
+  // per slice, without the slices' re-reads of x); with wide outputs (gate /
+  // up) the longer items balance worse over the CUs, 7% slower on the
+  // Llama-3-8B-shaped stack.
+  L.nsl = 0;
+  if (mfma && tn.mfma_xonce && mode == MODE_FUSED && ns >= 2 && ns <= 4 && d.K == 1 &&
+      (int64_t)d_sum <= 2 * (int64_t)shape->d_in) {
+    L.nsl = ns;
+    L.half = false;
+    L.smem_m = mfma_stacked_smem_bytes(L.jt, ns);
+    const int64_t tiles_m = (int64_t)n_groups * std::max(P.L.bound_m, P.L.bound_ms);
+    L.grid_m = round_up((int)std::max<int64_t>(std::min<int64_t>(tiles_m, tn.grid_cap), 1), 8);
+  }
   // One slot per request and one rank: every MFMA tile costs about the same,
   // and a launch over many problems deals each XCD whole problems, whose
   // adapters then sit in that XCD's L2 only.  (A single problem keeps the
@@ -220,8 +239,9 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
 // MFMA tiles (the long groups) first, then the VALU tiles.
 hipError_t launch_all(int mode, int dtype, const Launch &L, const ApplyArgs &a, hipStream_t stream) {
   if (L.jt > 0) {
-    hipError_t e = L.smax > 1 ? launch_mfma_stacked(L.jt, L.smax, a, L.grid_m, L.smem_m, stream)
-                              : launch_mfma(mode, L.jt, L.half, a, L.grid_m, L.smem_m, stream);
+    hipError_t e = L.nsl > 0    ? launch_mfma_sliced(L.jt, L.nsl, a, L.grid_m, L.smem_m, stream)
+                   : L.smax > 1 ? launch_mfma_stacked(L.jt, L.smax, a, L.grid_m, L.smem_m, stream)
+                                : launch_mfma(mode, L.jt, L.half, a, L.grid_m, L.smem_m, stream);
     if (e != hipSuccess) return e;
   }
   return launch_valu(mode, dtype, L.vec, a, L.grid_v, L.smem_v, stream);

@@ -216,5 +216,8 @@ hipError_t launch_mfma(int mode, int jt, bool half, const ApplyArgs &args, int g
 // a tile with several slots walks x once for all of them.
 size_t mfma_stacked_smem_bytes(int jt, int smax);
 hipError_t launch_mfma_stacked(int jt, int smax, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
+// Sliced launches with one slot per request and nsl (2 .. 4) slices a group:
+// one walk over x per row tile for every slice.  LDS: mfma_stacked_smem_bytes(jt, nsl).
+hipError_t launch_mfma_sliced(int jt, int nsl, const ApplyArgs &args, int grid, size_t smem, hipStream_t stream);
 
 }  // namespace lora

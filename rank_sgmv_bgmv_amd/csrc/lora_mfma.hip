@@ -296,9 +296,17 @@ struct StackCfg {
 // A tile whose rows carry 2 .. SMAX slots (fused mode): one walk over d_in,
 // the slots' intermediates in registers, then the expand of every output
 // block over every slot.
-template <int JT, int SMAX>
+//
+// SL (sliced launches, one slot per request): the "slots" are instead nsl
+// slices of a group that read the same x -- entries p0 .. p0 + nsl - 1 of the
+// group's problems `gp` -- each with its own A and B (the same adapter index
+// and scale), so one walk over x feeds every slice's intermediate; the expand
+// then writes each slice's whole output width to its own y.  `pr`, o_lo, o_hi
+// and d_out are unused then.
+template <int JT, int SMAX, bool SL = false>
 __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, int nrows, int o_lo, int o_hi,
-                                  int d_out, const Meta &M, uint16_t *stage) {
+                                  int d_out, const Meta &M, uint16_t *stage, const lora_problem *gp = nullptr,
+                                  int p0 = 0, int nsl = 0) {
   typedef StackCfg<JT, SMAX> C;
   constexpr int R = C::R, KC = C::KC, KS = C::KS, AST = C::AST, NAV = C::NAV, SST = C::SST;
   constexpr int NO = C::NO, OT = C::OT, BST = C::BST, NBV = C::NBV;
@@ -307,10 +315,19 @@ __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, in
   const int m = 16 * w + l16;  // this lane's tile row
   const bool row_ok = m < nrows;
   const bool wave_live = 16 * w < nrows;
-  const int d_in = a.d_in, nact = uniform(M.nact);
+  const int d_in = a.d_in, nact = SL ? nsl : uniform(M.nact);
   const int64_t trow = M.t[row_ok ? m : 0];
-  const uint16_t *__restrict__ xrow = static_cast<const uint16_t *>(pr.x) + trow * pr.ldx;
+  const lora_problem &px = SL ? gp[p0] : pr;  // the x every slot reads
+  const uint16_t *__restrict__ xrow = static_cast<const uint16_t *>(px.x) + trow * px.ldx;
   uint16_t *__restrict__ yrow = static_cast<uint16_t *>(pr.y) + trow * pr.ldy;
+  // A of every slot (a slice's own pool at the tile's one adapter when SL)
+  const uint16_t *Abase[SMAX];
+#pragma unroll
+  for (int g = 0; g < SMAX; ++g) {
+    const int gg = min(g, nact - 1);
+    Abase[g] = SL ? static_cast<const uint16_t *>(gp[p0 + gg].A) + (int64_t)M.a[0] * R * d_in
+                  : static_cast<const uint16_t *>(pr.A) + (int64_t)M.a[gg] * R * d_in;
+  }
 
   // ------------------------------------------------------------ shrink --
   f32x4 acc[SMAX][JT];
@@ -324,8 +341,9 @@ __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, in
 #pragma unroll
     for (int g = 0; g < SMAX; ++g) {
       const int gg = min(g, nact - 1);
-      const uint16_t *__restrict__ Ag = static_cast<const uint16_t *>(pr.A) + (int64_t)M.a[gg] * R * d_in;
-      const int rk = g < nact ? M.rk[gg] : 0;  // rows past the adapter's rank (or an unused slot) are zeros
+      const uint16_t *__restrict__ Ag = Abase[g];
+      // rows past the adapter's rank (or an unused slot) are zeros
+      const int rk = g < nact ? (SL ? M.rk[0] : M.rk[gg]) : 0;
 #pragma unroll
       for (int i = 0; i < NAV; ++i) {
         const int e = tid + i * kThreads;
@@ -386,7 +404,7 @@ __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, in
   uint2 v[SMAX][JT];
 #pragma unroll
   for (int g = 0; g < SMAX; ++g) {
-    const float sc = (row_ok && g < nact) ? M.sc[m][min(g, nact - 1)] : 0.f;
+    const float sc = (row_ok && g < nact) ? M.sc[m][SL ? 0 : min(g, nact - 1)] : 0.f;
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) {
       const f32x4 sv = acc[g][jt] * sc;
@@ -395,6 +413,120 @@ __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, in
   }
 
   // ------------------------------------------------------------ expand --
+  if constexpr (SL) {
+    // stages are (slice, output block), slice-major; each stage is a whole
+    // 128-output block of one slice's y, stored when the stage ends.  Each
+    // slice's width, B (at the tile's adapter) and y row are taken once here
+    // and picked by unrolled compares (no index known only at run time).
+    int dos[SMAX], nob[SMAX];
+    const uint16_t *Bb[SMAX];
+    uint16_t *Yb[SMAX];
+    int n_st = 0;
+#pragma unroll
+    for (int g = 0; g < SMAX; ++g) {
+      dos[g] = 0;
+#pragma unroll
+      for (int q = 0; q < LORA_MAX_SLICES; ++q)  // constant indices into the argument block
+        if (q == p0 + g) dos[g] = a.sd_out[q];
+      const lora_problem &pg = gp[p0 + min(g, nact - 1)];
+      Bb[g] = static_cast<const uint16_t *>(pg.B) + (int64_t)M.a[0] * dos[g] * R;
+      Yb[g] = static_cast<uint16_t *>(pg.y) + trow * pg.ldy;
+      nob[g] = g < nact ? (dos[g] + NO - 1) / NO : 0;
+      n_st += nob[g];
+    }
+    struct StageAt {
+      int g, ob, dout;
+      const uint16_t *B;
+      uint16_t *y;
+    };
+    auto stage_at = [&](int st) {
+      StageAt r{0, st, dos[0], Bb[0], Yb[0]};
+#pragma unroll
+      for (int q = 0; q + 1 < SMAX; ++q)
+        if (r.g == q && r.ob >= nob[q]) {
+          r.ob -= nob[q];
+          r.g = q + 1;
+          r.dout = dos[q + 1];
+          r.B = Bb[q + 1];
+          r.y = Yb[q + 1];
+        }
+      r.ob *= NO;
+      return r;
+    };
+    const int rk = M.rk[0];
+    uint4 br[NBV];
+    uint4 yc[OT / 2], yn[OT / 2];
+    f32x4 yacc[OT];
+    auto load_b = [&](const StageAt &sa) {
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) {
+        const int e = tid + i * kThreads;
+        const int row = e / (R / 8), c = 8 * (e % (R / 8));
+        br[i] = (sa.ob + row < sa.dout && c < rk) ? gload<uint4>(sa.B + (int64_t)(sa.ob + row) * R + c)
+                                                   : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto load_y = [&](const StageAt &sa, uint4(&yr)[OT / 2]) {
+#pragma unroll
+      for (int p = 0; p < OT / 2; ++p) {
+        const int o = sa.ob + 32 * p + 8 * kg;
+        yr[p] = (row_ok && o < sa.dout) ? gload<uint4>(sa.y + o) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    if (n_st > 0) {
+      const StageAt s0 = stage_at(0);
+      load_b(s0);
+      load_y(s0, yc);
+    }
+    for (int st = 0; st < n_st; ++st) {
+      const StageAt cur = stage_at(st);
+      lds_barrier();  // every wave is done reading the previous stage
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) {
+        const int e = tid + i * kThreads;
+        const int row = e / (R / 8);
+        const int lrow = (row & ~31) | (((row >> 2) & 1) << 4) | (((row >> 3) & 3) << 2) | (row & 3);
+        *reinterpret_cast<uint4 *>(stage + lrow * BST + 8 * (e % (R / 8))) = br[i];
+      }
+      lds_barrier();
+      if (st + 1 < n_st) {
+        const StageAt nx = stage_at(st + 1);
+        load_b(nx);
+        load_y(nx, yn);
+      }
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (wave_live) {
+#pragma unroll
+        for (int g = 0; g < SMAX; ++g) {
+          if (g == cur.g) {
+#pragma unroll
+            for (int ot = 0; ot < OT; ++ot) {
+#pragma unroll
+              for (int jt = 0; jt < JT; ++jt) {
+                const uint2 bv = *reinterpret_cast<const uint2 *>(stage + (16 * ot + l16) * BST + 16 * jt + 4 * kg);
+                yacc[ot] = mfma16(bv, v[g][jt], yacc[ot]);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < OT / 2; ++p) {
+        const int o = cur.ob + 32 * p + 8 * kg;
+        if (row_ok && o < cur.dout) {
+          const uint4 y0 = yc[p];
+          const f32x4 lo = yacc[2 * p], hi = yacc[2 * p + 1];
+          gstore(cur.y + o, make_uint4(pack_bf2(bf_lo(y0.x) + lo[0], bf_hi(y0.x) + lo[1]),
+                                       pack_bf2(bf_lo(y0.y) + lo[2], bf_hi(y0.y) + lo[3]),
+                                       pack_bf2(bf_lo(y0.z) + hi[0], bf_hi(y0.z) + hi[1]),
+                                       pack_bf2(bf_lo(y0.w) + hi[2], bf_hi(y0.w) + hi[3])));
+        }
+        yc[p] = yn[p];
+      }
+    }
+    return;
+  } else {
   // stages are (output block, slot), slot-minor, as in mfma_tile
   const int n_ob = (o_hi - o_lo + NO - 1) / NO;
   const int n_st = n_ob * nact;
@@ -475,6 +607,7 @@ __device__ void mfma_tile_stacked(const ApplyArgs &a, const lora_problem &pr, in
       for (int ot = 0; ot < OT; ++ot) yacc[ot] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  }
 }
 
 // ---------------------------------------------------------------- kernel --
@@ -538,6 +671,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   mfma_kernel_body<JT, 1, MODE_FUSED, SMAX, 1>(a);
 }
 
+// Sliced launches with one slot per request and 2 .. SMAX slices a group: one
+// item per row tile for all the group's slices.  When the slices read the same
+// x (the intended use, checked here per group) the tile walks x once for
+// every slice's intermediate; otherwise it walks it once per slice.  Held to
+// two waves per SIMD like the stacked build.
+template <int JT, int SMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void mfma_sliced_kernel(ApplyArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  Meta &M = *reinterpret_cast<Meta *>(smem);
+  uint16_t *stage = reinterpret_cast<uint16_t *>(smem + kMetaBytes);
+  const PlanHdr ph = read_plan_header(a);
+  if (!ph.ok) return;
+  const int n_m64 = ph.n_m, n_ms = ph.n_ms, n_active = ph.n_active;
+  // the plan's 48-row tiling under the same rule as mfma_kernel_body's
+  const bool small = (int64_t)n_m64 * a.n_problems > a.n_cu && (int64_t)n_ms * a.n_problems <= a.mfma_slots;
+  const int n_m = small ? n_ms : n_m64;
+  const int4 *tiles = small ? a.tiles_ms : a.tiles_m;
+  const int ns = a.ns;
+  walk_items((int64_t)n_m * a.n_problems, 1, [&](int64_t item) {
+    const int g = int(item / n_m);
+    const int tile = n_m - 1 - int(item - (int64_t)g * n_m);  // longest first, as in mfma_kernel_body
+    const lora_problem *gp = a.probs + (int64_t)g * ns;
+    const int4 td = gload<int4>(tiles + tile);
+    setup_rows(a, td, n_active, M);
+    if (M.nact > 0) {
+      const lora_problem q0 = gload<lora_problem>(gp);
+      bool same = true;
+      for (int p = 1; p < ns; ++p) {
+        const lora_problem q = gload<lora_problem>(gp + p);
+        same = same && q.x == q0.x && q.ldx == q0.ldx;
+      }
+      // one pass over every slice, or (different x) one pass per slice
+      const int passes = same ? 1 : ns;
+      for (int p = 0; p < passes; ++p)
+        mfma_tile_stacked<JT, SMAX, true>(a, q0, td.z, 0, 0, 0, M, stage, gp, same ? 0 : p, same ? ns : 1);
+    }
+  }, a.mfma_uniform != 0);
+}
+
 // Launch one instantiation; the first launch lifts its dynamic-LDS limit to
 // the 160 KB a gfx950 workgroup may use.
 template <int JT, int HS, int M, int NSL>
@@ -547,6 +719,16 @@ hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t str
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   (void)lds_limit_raised;
   hipLaunchKernelGGL((mfma_kernel<JT, HS, M, NSL>), dim3(grid), dim3(kThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int JT, int SMAX>
+hipError_t launch_sliced(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  static const bool lds_limit_raised =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_sliced_kernel<JT, SMAX>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+  (void)lds_limit_raised;
+  hipLaunchKernelGGL((mfma_sliced_kernel<JT, SMAX>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -635,6 +817,24 @@ hipError_t launch_mfma_stacked(int jt, int smax, const ApplyArgs &a, int grid, s
     case 128 + 2: return launch_stacked<8, 2>(a, grid, smem, stream);
     case 128 + 3: return launch_stacked<8, 3>(a, grid, smem, stream);
     case 128 + 4: return launch_stacked<8, 4>(a, grid, smem, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_sliced(int jt, int nsl, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
+  switch (jt * 16 + nsl) {
+    case 16 + 2: return launch_sliced<1, 2>(a, grid, smem, stream);
+    case 16 + 3: return launch_sliced<1, 3>(a, grid, smem, stream);
+    case 16 + 4: return launch_sliced<1, 4>(a, grid, smem, stream);
+    case 32 + 2: return launch_sliced<2, 2>(a, grid, smem, stream);
+    case 32 + 3: return launch_sliced<2, 3>(a, grid, smem, stream);
+    case 32 + 4: return launch_sliced<2, 4>(a, grid, smem, stream);
+    case 64 + 2: return launch_sliced<4, 2>(a, grid, smem, stream);
+    case 64 + 3: return launch_sliced<4, 3>(a, grid, smem, stream);
+    case 64 + 4: return launch_sliced<4, 4>(a, grid, smem, stream);
+    case 128 + 2: return launch_sliced<8, 2>(a, grid, smem, stream);
+    case 128 + 3: return launch_sliced<8, 3>(a, grid, smem, stream);
+    case 128 + 4: return launch_sliced<8, 4>(a, grid, smem, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -83,6 +83,11 @@ GRID = {
     # widths that are not a multiple of 8: scalar path
     "odd_widths_bf16": dict(dtype=W.BF16, n=4, r=16, d_in=64, d_outs=(100, 36, 20), groups=2,
                             batch=dict(S=7, K=2, min_len=0, max_len=12)),
+    # one slot per request on the MFMA path: one walk over x for all slices of a tile
+    "four_slices_prefill_r16": dict(dtype=W.BF16, n=5, r=16, d_in=320, d_outs=(128, 64, 192, 64), groups=2,
+                                    batch=dict(S=5, K=1, min_len=40, max_len=120, with_scale=True, p_empty=0.1)),
+    "two_slices_prefill_r128": dict(dtype=W.BF16, n=4, r=128, d_in=264, d_outs=(384, 136), groups=2,
+                                    batch=dict(S=4, K=1, min_len=50, max_len=150)),
     # many slices, one of them narrow
     "eight_slices": dict(dtype=W.BF16, n=3, r=16, d_in=128, d_outs=(64, 128, 8, 64, 256, 64, 64, 128), groups=1,
                          batch=dict(S=5, K=1, min_len=1, max_len=40)),
@@ -184,3 +189,50 @@ def test_sliced_c4_qkv_sampled(orc):
     multi = _run_multi_per_slice([g], db, plan)
     for p in range(3):
         assert np.array_equal(sliced[0][p], multi[0][p]), f"slice {p}"
+
+
+def test_sliced_distinct_x(orc):
+    """The call allows each slice its own x.  Three groups of three slices on
+    the MFMA path: one whose slices share one x (one walk over x for all three),
+    one whose slices each read another x, and one where two of three share.
+    Each slice against the oracle on its own x, and bit for bit against one
+    launch per slice."""
+    rng = np.random.default_rng(5300)
+    n, r, d_in, d_outs = 6, 32, 256, (256, 128, 96)
+    batch = W.random_batch(rng, n=n, S=5, K=1, min_len=30, max_len=120, with_scale=True, p_empty=0.1)
+    assert batch.T >= 128  # the MFMA path
+    xs = [W.make_xy(rng, W.BF16, batch.T, d_in, 8)[0] for _ in range(4)]
+    xs_dev = [to_dev(x, W.BF16) for x in xs]
+    x_of = [(0, 0, 0), (1, 2, 3), (1, 1, 2)]  # which x each slice of each group reads
+    groups = []
+    for gi in range(3):
+        pools = [W.make_pool(rng, W.BF16, n, r, d_in, d) for d in d_outs]
+        ys = [W.make_xy(rng, W.BF16, batch.T, 8, d)[1] for d in d_outs]
+        groups.append((pools, ys, [(to_dev(p.A, W.BF16), to_dev(p.B, W.BF16)) for p in pools],
+                       [to_dev(y, W.BF16) for y in ys]))
+    db = dev_batch(batch)
+    plan = L.new_workspace(db, n, DEV)
+    L.lora_plan_build(db, n, plan)
+    rows = [(A, B, xs_dev[x_of[gi][p]], yd)
+            for gi, (_, _, AB, yds) in enumerate(groups) for p, ((A, B), yd) in enumerate(zip(AB, yds))]
+    table, aligned = L.problems_table(rows, DEV)
+    A0, B0 = groups[0][2][0]
+    L.lora_apply_sliced(L.Pool(A0, B0), db, plan, table, list(d_outs), aligned)
+    torch.cuda.synchronize()
+    sliced = [[from_dev(yd, W.BF16) for yd in g[3]] for g in groups]
+    for gi, (pools, ys, _, _) in enumerate(groups):
+        for p, (pool, y0) in enumerate(zip(pools, ys)):
+            case = W.Case(f"group{gi}_slice{p}", W.BF16, batch, pool, xs[x_of[gi][p]], y0)
+            y_ref, touched, _, _ = orc.apply_case(case)
+            assert_parity(case, sliced[gi][p], y_ref, touched, what=case.name)
+    for gi, (pools, ys, AB, yds) in enumerate(groups):
+        for yd, y in zip(yds, ys):
+            yd.copy_(to_dev(y, W.BF16))
+    for p in range(len(d_outs)):
+        probs = [(g[2][p][0], g[2][p][1], xs_dev[x_of[gi][p]], g[3][p]) for gi, g in enumerate(groups)]
+        t, al = L.problems_table(probs, DEV)
+        L.lora_apply_multi(L.Pool(groups[0][2][p][0], groups[0][2][p][1]), db, plan, t, al)
+    torch.cuda.synchronize()
+    for gi, g in enumerate(groups):
+        for p, yd in enumerate(g[3]):
+            assert np.array_equal(sliced[gi][p], from_dev(yd, W.BF16)), f"group {gi} slice {p}: sliced != per-slice"
