@@ -199,6 +199,20 @@ struct MergeArgs {
 bool merge_mfma_eligible(const MergeArgs &a, int dtype);
 hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t stream);
 
+// Lift a kernel's dynamic-LDS limit to `bytes` (at most what gfx950 allows
+// beside the kernel's static LDS); called once per kernel, before its first
+// launch.  A refused attribute leaves the limit as it was and is cleared, so
+// that it is not reported as the error of the launch that follows.
+inline bool raise_lds_limit(const void *kernel, size_t bytes) {
+  hipFuncAttributes at;
+  size_t stat = 0;
+  if (hipFuncGetAttributes(&at, kernel) == hipSuccess) stat = at.sharedSizeBytes;
+  const size_t lim = bytes + stat > size_t(kMaxLdsBytes) ? size_t(kMaxLdsBytes) - stat : bytes;
+  const bool ok = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lim)) == hipSuccess;
+  (void)hipGetLastError();
+  return ok;
+}
+
 size_t valu_smem_bytes(int kr_max);
 // MFMA kernel LDS per workgroup; `half`: the half-size stages (ranks 64 / 128 only).
 size_t mfma_smem_bytes(int jt, int slots, bool half);

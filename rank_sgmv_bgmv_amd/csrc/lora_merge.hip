@@ -252,8 +252,7 @@ __global__ __launch_bounds__(kThreads) void merge_valu_kernel(MergeArgs a) {
 template <int KSR, int NE>
 hipError_t launch_mfma_ksr(const MergeArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&merge_mfma_kernel<KSR, NE>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+      raise_lds_limit(reinterpret_cast<const void *>(&merge_mfma_kernel<KSR, NE>), kMaxLdsBytes);
   (void)lds_limit_raised;
   hipLaunchKernelGGL((merge_mfma_kernel<KSR, NE>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();

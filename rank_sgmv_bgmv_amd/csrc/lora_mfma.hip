@@ -715,8 +715,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 template <int JT, int HS, int M, int NSL>
 hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_kernel<JT, HS, M, NSL>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+      raise_lds_limit(reinterpret_cast<const void *>(&mfma_kernel<JT, HS, M, NSL>), kMaxLdsBytes);
   (void)lds_limit_raised;
   hipLaunchKernelGGL((mfma_kernel<JT, HS, M, NSL>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
@@ -725,8 +724,7 @@ hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t str
 template <int JT, int SMAX>
 hipError_t launch_sliced(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_sliced_kernel<JT, SMAX>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+      raise_lds_limit(reinterpret_cast<const void *>(&mfma_sliced_kernel<JT, SMAX>), kMaxLdsBytes);
   (void)lds_limit_raised;
   hipLaunchKernelGGL((mfma_sliced_kernel<JT, SMAX>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
@@ -735,8 +733,7 @@ hipError_t launch_sliced(const ApplyArgs &a, int grid, size_t smem, hipStream_t 
 template <int JT, int SMAX>
 hipError_t launch_stacked(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_stacked_kernel<JT, SMAX>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+      raise_lds_limit(reinterpret_cast<const void *>(&mfma_stacked_kernel<JT, SMAX>), kMaxLdsBytes);
   (void)lds_limit_raised;
   hipLaunchKernelGGL((mfma_stacked_kernel<JT, SMAX>), dim3(grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();

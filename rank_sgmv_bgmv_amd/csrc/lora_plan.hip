@@ -506,8 +506,7 @@ __global__ __launch_bounds__(kPlanSmallThreads) void plan_kernel_small(PlanView 
 
 hipError_t launch_plan(const PlanView &P, size_t lds_bytes, const int *seg_off, const int *idx, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(plan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          int(kPlanLdsBudget)) == hipSuccess;
+      raise_lds_limit(reinterpret_cast<const void *>(plan_kernel), kPlanLdsBudget);
   (void)lds_limit_raised;
   if (P.S <= 64)
     hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(kPlanSmallThreads), 0, stream, P, seg_off, idx);

@@ -388,8 +388,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
 template <typename T, bool VEC, int M, int NSL>
 hipError_t launch_one(const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   static const bool lds_limit_raised =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&valu_kernel<T, VEC, M, NSL>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+      raise_lds_limit(reinterpret_cast<const void *>(&valu_kernel<T, VEC, M, NSL>), kMaxLdsBytes);
   (void)lds_limit_raised;
   hipLaunchKernelGGL((valu_kernel<T, VEC, M, NSL>), dim3(grid), dim3(kValuThreads), smem, stream, a);
   return hipGetLastError();
