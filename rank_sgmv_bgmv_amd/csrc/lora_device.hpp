@@ -130,6 +130,15 @@ template <> struct VOps<uint16_t, true> {
     acc = fmaf(v1.z, bf_lo(b.w), acc); acc = fmaf(v1.w, bf_hi(b.w), acc);
     return acc;
   }
+  // y + d, rounded once (d: 8 floats)
+  static __device__ __forceinline__ V add(V y, const float *d) {
+    uint4 o;
+    o.x = pack_bf2(bf_lo(y.x) + d[0], bf_hi(y.x) + d[1]);
+    o.y = pack_bf2(bf_lo(y.y) + d[2], bf_hi(y.y) + d[3]);
+    o.z = pack_bf2(bf_lo(y.z) + d[4], bf_hi(y.z) + d[5]);
+    o.w = pack_bf2(bf_lo(y.w) + d[6], bf_hi(y.w) + d[7]);
+    return o;
+  }
   static __device__ __forceinline__ void add_store(uint16_t *p, const float *d) {
     uint4 y = load(p);
     const float4 d0 = *reinterpret_cast<const float4 *>(d);
@@ -167,6 +176,9 @@ template <> struct VOps<float, true> {
   static __device__ __forceinline__ float dotf(const float *v, V b, float acc) {
     const float4 a = *reinterpret_cast<const float4 *>(v);
     return dot(a, b, acc);
+  }
+  static __device__ __forceinline__ V add(V y, const float *d) {
+    return make_float4(y.x + d[0], y.y + d[1], y.z + d[2], y.w + d[3]);
   }
   static __device__ __forceinline__ void add_store(float *p, const float *d) {
     float4 y = load(p);

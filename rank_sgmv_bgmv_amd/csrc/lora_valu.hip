@@ -219,11 +219,125 @@ __device__ void valu_expand(const ApplyArgs &a, const lora_problem &pr, int m0, 
   }
 }
 
+// Coalesced expand (vector path): B is [d_out][r]; the tile's slots use VPR
+// 16-byte vectors of each row (VPR = 2, 4, 8 or 16: ranks 16 .. 128 in bf16,
+// 8 .. 64 in fp32).  A wave's load instruction reads RPI = 64 / VPR whole
+// rows -- lane l takes vector l % VPR of row l / VPR -- so, when the pool is
+// stored at the tile's rank, every instruction reads 1 KB of consecutive
+// memory (a lane reading a run of whole rows touches up to 64 cache lines
+// per instruction).  Each lane multiplies its vector with the matching rank
+// slice of the intermediate (from LDS); the VPR lanes of a row add their
+// partial sums by lane exchanges; the row sums go through a per-wave LDS
+// stage so that each lane updates 16 consecutive bytes of y with one load and
+// one store.  A wave's round covers NI instructions (NI * RPI outputs).
+constexpr int kExpandStage = 1024;  // fp32 staging slots per wave
+constexpr size_t expand_stage_offset(int kr_max) { return (size_t(kRowBlock) * kr_max * 4 + 15) & ~size_t(15); }
+
+template <typename T, int MB, int NI, int MODE>
+__device__ void valu_expand_co(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
+                               const InterT<T, true, MODE> *s_v, int o_lo, int o_hi, int d_out, int vpr) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  typedef VOps<T, true> O;
+  typedef typename O::V V;
+  typedef InterT<T, true, MODE> IT;
+  constexpr int E = O::E;
+  static_assert(MB * NI * 32 <= kExpandStage, "a round's sums fit the stage (VPR >= 2)");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane & (vpr - 1), rl = lane / vpr;
+  const int rpi = 64 / vpr, wrows = NI * rpi, yv_lanes = wrows / E;
+  const int r = a.r, KR = a.kr_max, nact = uniform(M.nact);
+  const uint32_t brow_bytes = uint32_t(r) * sizeof(T);
+  float *so = reinterpret_cast<float *>(smem + kMetaBytes + expand_stage_offset(KR)) + w * kExpandStage;
+  T *yrow[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+    yrow[m] = static_cast<T *>(pr.y) + (int64_t)uniform(M.t[m0 + (m < nb ? m : 0)]) * pr.ldy;
+  for (int o0 = o_lo + w * wrows; o0 < o_hi; o0 += (kValuThreads / 64) * wrows) {
+    // this lane's y vector (outputs oy .. oy+E-1), loaded first; lanes past
+    // the round's outputs load a valid vector and store nothing
+    const int oy = o0 + lane * E;
+    const bool yok = lane < yv_lanes && oy < o_hi;
+    const uint32_t yoff = uint32_t(min(oy, o_hi - E)) * sizeof(T);
+    V yv[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) yv[m] = gload_at<V>(yrow[m], yoff);
+    float acc[MB][NI];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[m][i] = 0.f;
+    for (int kk = 0; kk < nact; ++kk) {
+      const T *Bk = static_cast<const T *>(pr.B) + (int64_t)uniform(M.a[kk]) * d_out * r;
+      V bv[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        bv[i] = gload_at<V>(Bk, uint32_t(min(o0 + i * rpi + rl, o_hi - 1)) * brow_bytes + uint32_t(q) * 16u);
+      // vectors past the adapter's rank hold padding: never used (the
+      // intermediate is zero there, and the padding need not be finite)
+      if (q * E >= uniform(M.rk[kk])) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) bv[i] = O::zero();
+      }
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m < nb) {
+          const IT *vp = s_v + m * KR + kk * r + q * E;
+          if constexpr (sizeof(IT) == 2) {
+            const V vv = *reinterpret_cast<const V *>(vp);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[m][i] = O::dot(vv, bv[i], acc[m][i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) acc[m][i] = O::dotf(vp, bv[i], acc[m][i]);
+          }
+        }
+      }
+    }
+    // row sums over the row's vpr lanes; lane q stages the sums of the
+    // instructions i with i % vpr == q
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m < nb) {
+        for (int bit = 1; bit < vpr; bit <<= 1) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) acc[m][i] += __shfl_xor(acc[m][i], bit);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          if ((i & (vpr - 1)) == q) so[m * wrows + i * rpi + rl] = acc[m][i];
+      }
+    }
+    // the stage is the wave's own: order its writes before its reads (and,
+    // below, those reads before the next round's writes)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m < nb && yok) {
+        float d[E];
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const float4 f = *reinterpret_cast<const float4 *>(so + m * wrows + lane * E + e);
+          d[e] = f.x;
+          d[e + 1] = f.y;
+          d[e + 2] = f.z;
+          d[e + 3] = f.w;
+        }
+        gstore_at(yrow[m], yoff, O::add(yv[m], d));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+}
+
 // Outputs per block: rows of about 64 bytes per lane (counting the rank the
 // tile uses), never more than the vector width, which divides d_out on the vector path (so a block never
 // straddles the end of a row).  Blocks per round: about 16 B vectors per lane
 // (8 with four rows).  The scalar path takes one output per thread.
-template <typename T, bool VEC, int MB, int MODE>
+template <typename T, bool VEC, int MB, int MODE, bool CO>
 __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m0, int nb, const Meta &M,
                                const InterT<T, VEC, MODE> *s_v, int o_lo, int o_hi, int d_out) {
   constexpr int E = VOps<T, VEC>::E;
@@ -237,6 +351,16 @@ __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m
     int kr = 1;
     for (int kk = 0; kk < M.nact; ++kk) kr = max(kr, M.rk[kk]);
     const int vpr = (uniform(kr) + E - 1) / E;
+    // Tiles whose rows stack several adapters take the coalesced expand when
+    // their slots use 2 .. 16 vectors of each row of B (measured: 5% faster on
+    // the stacked decode; one-adapter tiles run faster on the runs below)
+    if constexpr (CO) {
+      constexpr int NI = MB >= 4 ? 8 : 16;
+      if (M.nact >= 2 && vpr >= 2 && vpr <= NI && (vpr & (vpr - 1)) == 0 && vpr * E <= a.r) {
+        valu_expand_co<T, MB, NI, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out, vpr);
+        return;
+      }
+    }
     const int row_bytes = vpr * E * int(sizeof(T));
     const int rt = min(max(64 / row_bytes, 1), E);
     int nblk = expand_nvb<MB, sizeof(InterT<T, VEC, MODE>)>() / (rt * vpr);
@@ -258,7 +382,7 @@ __device__ void valu_expand_rt(const ApplyArgs &a, const lora_problem &pr, int m
 }
 
 // Rows row_lo .. row_hi-1 of a tile, in blocks of kRowBlock rows.
-template <typename T, bool VEC, int MODE>
+template <typename T, bool VEC, int MODE, bool CO>
 __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int row_lo, int row_hi, int o_lo, int o_hi,
                           int d_out, Meta &M, InterT<T, VEC, MODE> *s_v) {
   const int tid = threadIdx.x;
@@ -280,9 +404,9 @@ __device__ void valu_tile(const ApplyArgs &a, const lora_problem &pr, int row_lo
     }
     if (MODE == MODE_SHRINK) continue;
     lds_barrier();  // the intermediate of this row block is complete
-    if (nb <= 1) valu_expand_rt<T, VEC, 1, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
-    else if (nb <= 2) valu_expand_rt<T, VEC, 2, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
-    else valu_expand_rt<T, VEC, 4, MODE>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
+    if (nb <= 1) valu_expand_rt<T, VEC, 1, MODE, CO>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
+    else if (nb <= 2) valu_expand_rt<T, VEC, 2, MODE, CO>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
+    else valu_expand_rt<T, VEC, 4, MODE, CO>(a, pr, m0, nb, M, s_v, o_lo, o_hi, d_out);
     lds_barrier();  // before the next row block overwrites the intermediate
   }
 }
@@ -375,7 +499,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(ApplyArgs a) {
       row_hi = setup_from_record(a, cur.word, M);
     }
     if (M.nact > 0 && row_lo < row_hi && (MODE == MODE_SHRINK || o_lo < o_hi))
-      valu_tile<T, VEC, MODE>(a, cur.pr, row_lo, row_hi, o_lo, o_hi, c.d_out, M, s_v);
+      valu_tile<T, VEC, MODE, MODE == MODE_FUSED && NSL == 1>(a, cur.pr, row_lo, row_hi, o_lo, o_hi, c.d_out, M, s_v);
     lds_barrier();
     it = nx;
     i += per_xcd;
@@ -410,7 +534,9 @@ hipError_t launch_mode(int mode, const ApplyArgs &a, int grid, size_t smem, hipS
 
 }  // namespace
 
-size_t valu_smem_bytes(int kr_max) { return kMetaBytes + size_t(kRowBlock) * kr_max * 4; }
+size_t valu_smem_bytes(int kr_max) {
+  return kMetaBytes + expand_stage_offset(kr_max) + size_t(kValuThreads / 64) * kExpandStage * 4;
+}
 
 hipError_t launch_valu(int mode, int dtype, bool vec, const ApplyArgs &a, int grid, size_t smem, hipStream_t stream) {
   if (dtype == LORA_F32)
