@@ -561,9 +561,37 @@ def calibration(dev, reps=20):
     read_ms = timed(lambda: src.sum(), True)
     floor_ms = timed(lambda: tiny.fill_(0.0), False)
     del src, dst
+    # The decode headline's adapter stream without its arithmetic
+    # (lora_calib_gather_read, include/lora_calib.h): 2688 blocks of 128 KB
+    # (one rank-16 4096-wide A or B each, about as many as the 32-layer launch
+    # reads) at distinct random block-aligned places of a 4 GiB pool, read (a)
+    # one block per workgroup, (b) two per workgroup with a barrier between
+    # them and an 8 KB slice read and written back, as a decode work item
+    # reads A, then B, and updates one row of y.
+    import rank_sgmv_bgmv_amd as L
+    blk, n_blk, pool_bytes = 128 << 10, 2688, 4 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    pick = np.random.default_rng(7).choice(pool_bytes // blk, size=n_blk, replace=False)
+    off = torch.from_numpy(pick.astype(np.int64) * blk).to(dev)
+    assert int(off.max()) + blk <= pool_bytes
+    sink = torch.empty(n_blk, dtype=torch.int32, device=dev)
+    rmw = torch.zeros(n_blk // 2 * 8192, dtype=torch.uint8, device=dev)
+    one_ms = timed(lambda: L.lora_calib_gather_read(pool, off, 1, blk, sink), True)
+    pair_ms = timed(lambda: L.lora_calib_gather_read(pool, off, 2, blk, sink, rmw=rmw, rmw_bytes=8192), True)
+    del pool, rmw
+    pair_bytes = n_blk * blk + 2 * (n_blk // 2) * 8192
     return {"copy_1GiB_GBps": 2 * n / (copy_ms * 1e-3) / 1e9, "read_1GiB_GBps": n / (read_ms * 1e-3) / 1e9,
+            "gather_read": {"what": f"{n_blk} blocks of 128 KB at random places of a 4 GiB pool, one workgroup each",
+                            "bytes": n_blk * blk, "us": round(one_ms * 1e3, 3),
+                            "GBps": n_blk * blk / (one_ms * 1e-3) / 1e9},
+            "decode_skeleton": {"what": f"{n_blk // 2} workgroups, each reading two of those blocks with a barrier "
+                                        "between them and reading and writing back 8 KB (a decode work item's "
+                                        "A, B and y row, no arithmetic)",
+                                "bytes": pair_bytes, "us": round(pair_ms * 1e3, 3),
+                                "GBps": pair_bytes / (pair_ms * 1e-3) / 1e9},
             "empty_kernel_floor_us": round(floor_ms * 1e3, 3),
-            "note": "torch copy_ and sum after a cache flush; medians of HIP-event times"}
+            "note": "torch copy_ and sum, and the library's gather-read probe, each after a cache flush; medians "
+                    "of HIP-event times"}
 
 
 def copy_calibration(dev, mib=256, reps=5):
@@ -754,6 +782,9 @@ def main():
         log("cpu baseline ...")
         cpu = cpu_baseline(stack)
 
+    if head is None and not variants:  # calibration alone
+        print(json.dumps({"calibration": calib}))
+        return
     if head is None:  # a partial run: report the first variant as the line
         name, head = next(iter(variants.items()))
     apply = head.get("apply") or {}
@@ -780,7 +811,8 @@ def main():
                      "kernel": "valu_kernel<bf16, vec, fused> (shrink + expand of every decode tile, one launch for "
                                "all 32 layers)",
                      "bytes_per_launch": head.get("apply_bytes_per_launch"), "avg_launch_us": apply.get("mean_us"),
-                     "median_launch_us": apply.get("median_us"), "flushed": head.get("flushed")},
+                     "median_launch_us": apply.get("median_us"), "flushed": head.get("flushed"),
+                     "same_traffic_no_arithmetic_GBps": (calib or {}).get("decode_skeleton", {}).get("GBps")},
         "cpu_baseline": cpu,
         "calibration": calib,
         "headline": head,

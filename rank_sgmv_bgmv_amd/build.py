@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "liblora_hip.so")
-SOURCES = ["lora_api.hip", "lora_plan.hip", "lora_valu.hip", "lora_mfma.hip", "lora_merge.hip"]
+SOURCES = ["lora_api.hip", "lora_plan.hip", "lora_valu.hip", "lora_mfma.hip", "lora_merge.hip", "lora_calib.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

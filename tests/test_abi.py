@@ -11,12 +11,15 @@ import rank_sgmv_bgmv_amd as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lora.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "lora_calib.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(lora_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert len(names) >= 12, names
     for name in names:
-        assert hasattr(lib, name), f"{name} declared in lora.h but not exported"
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
 
 
 def test_exported_symbols_match_binding(lib):
@@ -204,3 +207,18 @@ def test_sliced_table_layout_and_checks():
     shape = L.Pool(*g0[0][:2])
     with pytest.raises(L.LoraError):  # 4 rows are not whole groups of 3 slices
         L.lora_apply_sliced(shape, None, None, table, [32, 16, 16])
+
+
+def test_calib_gather_read_host_checks(lib):
+    f = lib.lora_calib_gather_read
+    ok = dict(pool=FAKE, off=FAKE, n=4, bpg=2, bb=1 << 17, rmw=None, rb=0, sink=FAKE * 2)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["pool"], a["off"], a["n"], a["bpg"], a["bb"], a["rmw"], a["rb"], a["sink"], None)
+
+    assert call(pool=None) == -1 and call(off=None) == -1 and call(sink=None) == -1 and call(n=-1) == -1
+    assert call(bpg=0) == -2 and call(bb=0) == -2 and call(bb=16384) == -2
+    assert call(rmw=FAKE * 3, rb=0) == -2 and call(rmw=FAKE * 3, rb=1000) == -2
+    assert call(rmw=FAKE * 3, rb=5 * 4096) == -2
+    assert call(n=0) == 0 and call(n=0, rmw=FAKE * 3, rb=8192) == 0  # nothing to read: nothing launched
