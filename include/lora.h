@@ -28,11 +28,15 @@
  * Memory and ownership.  Every pointer in a struct or argument below is a
  * DEVICE pointer unless its comment says "host".  All buffers are allocated
  * and owned by the caller; the library allocates and frees nothing and is
- * re-entrant.  The only state it keeps between calls is looked up once and
- * never changes: each device's compute-unit count, the kernels' LDS limit,
- * the tuning values read from the environment at the first call, and each
+ * re-entrant.  The only state it keeps between calls is looked up or created
+ * once and never changes: each device's compute-unit count, the kernels' LDS
+ * limit, the tuning values read from the environment at the first call, each
  * device's address of the fixed plan array that lora_apply_noalloc uses (a
- * static device array of the library, not an allocation).  Every
+ * static device array of the library, not an allocation), and, created at the
+ * first multi-problem launch with prefill tiles on a device, one extra stream
+ * and two events of that device (such launches run their decode tiles on it,
+ * beside the prefill tiles, and the caller's stream waits for both; the
+ * launch stays asynchronous and can be captured in a graph).  Every
  * compute call is asynchronous on the given stream and never synchronizes,
  * except lora_read_device_errors.
  * x and y must not overlap; v must overlap neither x nor y.

@@ -4,8 +4,9 @@ builders bench.py uses), against the fp64 oracle on sampled rows:
 
   * the Llama-3-8B-shaped stack: 4 lora_apply_multi launches of 64, 64, 64 and
     32 problems on one plan (about three VALU work items per workgroup), the
-    sliced launches of the shared-x stack, and the 224 per-projection calls
-    captured in a HIP graph;
+    sliced launches of the shared-x stack, the 224 per-projection calls
+    captured in a HIP graph, and the 4 launches captured in one (their second
+    stream included);
   * the merge of one rank-64 adapter into 228 FLUX-sized 3072 x 3072 weights
     (about 16 work items per workgroup);
   * the decode batch through 32 q_proj pools of 1000 adapters.
@@ -132,6 +133,65 @@ def test_c4_per_projection_calls_in_a_graph(orc):
         torch.cuda.synchronize()
         for k, ((_, p), want) in enumerate(zip(calls, eager)):
             assert torch.equal(p.y.view(torch.int16), want.view(torch.int16)), f"replay {rep}, call {k}"
+    del graph, st, plan, eager, y0
+    _free()
+
+
+def test_c4_multi_launches_in_a_graph_and_against_single_calls():
+    """The stack's 4 multi-problem launches run the decode tiles' kernel on a
+    second stream beside the prefill tiles' kernel.  Captured in one HIP graph
+    (the fork and join are part of the capture), every replay, with eager work
+    and synchronisations between them, must equal the eager launches bit for
+    bit, and both must equal one lora_apply_planned call per projection (one
+    stream) bit for bit on the checked projections."""
+    st = WD.c4_stack(DEV)
+    db = dev_batch(st.batch)
+    plan = L.new_workspace(db, st.n, DEV)
+    L.lora_plan_build(db, st.n, plan)
+    launches, projs_all = [], []
+    for _, _, projs in st.groups:
+        table, aligned = L.problems_table([(p.A, p.B, p.x, p.y) for p in projs], DEV)
+        launches.append((L.Pool(projs[0].A, projs[0].B), table, aligned))
+        projs_all += projs
+    y0 = [p.y.clone() for p in projs_all]
+
+    def reset():
+        for p, y in zip(projs_all, y0):
+            p.y.copy_(y)
+
+    def run_multi():
+        for shape, table, aligned in launches:
+            L.lora_apply_multi(shape, db, plan, table, aligned)
+
+    run_multi()
+    torch.cuda.synchronize()
+    eager = [p.y.clone() for p in projs_all]
+    chk = sorted({0, 63, 64, 127, 128, 191, 192, 223})
+    reset()
+    for i in chk:
+        p = projs_all[i]
+        L.lora_apply_planned(L.Pool(p.A, p.B), db, plan, p.x, p.y)
+    torch.cuda.synchronize()
+    for i in chk:
+        assert torch.equal(projs_all[i].y.view(torch.int16), eager[i].view(torch.int16)), f"single call {i}"
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run_multi()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        L.lora_plan_build(db, st.n, plan)  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (p, want) in enumerate(zip(projs_all, eager)):
+            assert torch.equal(p.y.view(torch.int16), want.view(torch.int16)), f"replay {rep}, problem {k}"
     del graph, st, plan, eager, y0
     _free()
 
