@@ -578,6 +578,9 @@ def calibration(dev, reps=20):
     rmw = torch.zeros(n_blk // 2 * 8192, dtype=torch.uint8, device=dev)
     one_ms = timed(lambda: L.lora_calib_gather_read(pool, off, 1, blk, sink), True)
     pair_ms = timed(lambda: L.lora_calib_gather_read(pool, off, 2, blk, sink, rmw=rmw, rmw_bytes=8192), True)
+    # the same with at most two workgroups per compute unit, as the decode kernel runs
+    pair2_ms = timed(lambda: L.lora_calib_gather_read(pool, off, 2, blk, sink, rmw=rmw, rmw_bytes=8192,
+                                                      lds_bytes=65536), True)
     del pool, rmw
     pair_bytes = n_blk * blk + 2 * (n_blk // 2) * 8192
     return {"copy_1GiB_GBps": 2 * n / (copy_ms * 1e-3) / 1e9, "read_1GiB_GBps": n / (read_ms * 1e-3) / 1e9,
@@ -588,7 +591,9 @@ def calibration(dev, reps=20):
                                         "between them and reading and writing back 8 KB (a decode work item's "
                                         "A, B and y row, no arithmetic)",
                                 "bytes": pair_bytes, "us": round(pair_ms * 1e3, 3),
-                                "GBps": pair_bytes / (pair_ms * 1e-3) / 1e9},
+                                "GBps": pair_bytes / (pair_ms * 1e-3) / 1e9,
+                                "two_per_cu_us": round(pair2_ms * 1e3, 3),
+                                "two_per_cu_GBps": pair_bytes / (pair2_ms * 1e-3) / 1e9},
             "empty_kernel_floor_us": round(floor_ms * 1e3, 3),
             "note": "torch copy_ and sum, and the library's gather-read probe, each after a cache flush; medians "
                     "of HIP-event times"}
@@ -812,7 +817,7 @@ def main():
                                "all 32 layers)",
                      "bytes_per_launch": head.get("apply_bytes_per_launch"), "avg_launch_us": apply.get("mean_us"),
                      "median_launch_us": apply.get("median_us"), "flushed": head.get("flushed"),
-                     "same_traffic_no_arithmetic_GBps": (calib or {}).get("decode_skeleton", {}).get("GBps")},
+                     "same_traffic_no_arithmetic_GBps": (calib or {}).get("decode_skeleton", {}).get("two_per_cu_GBps")},
         "cpu_baseline": cpu,
         "calibration": calib,
         "headline": head,

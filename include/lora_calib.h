@@ -30,7 +30,10 @@ extern "C" {
  * them: block k of group g starts at byte offset off[g * blocks_per_group + k]
  * of `pool`.  With rmw != NULL the workgroup also reads rmw_bytes bytes at
  * rmw + g * rmw_bytes before its last block and writes the same bytes back
- * after it (the values are unchanged).  It writes one 32-bit word,
+ * after it (the values are unchanged).  Each workgroup reserves lds_bytes of
+ * LDS (0 .. 65536) that it does not use, which limits how many workgroups
+ * share a compute unit (65536: two, as many as the decode kernel fits).  It
+ * writes one 32-bit word,
  * sink[g] = the XOR of the 32-bit words of its blocks, so that no load can be
  * dropped.
  *   pool         device, read only; every block lies inside it
@@ -42,12 +45,12 @@ extern "C" {
  *   sink         device, n_groups words, written
  * Returns LORA_EINVAL for NULL pool, off or sink, or n_groups < 0;
  * LORA_ESHAPE for blocks_per_group < 1, a block size that is not a positive
- * multiple of 32768, or (rmw given) an rmw_bytes other than those four;
- * LORA_EHIP when the launch fails.  n_groups == 0 launches
+ * multiple of 32768, (rmw given) an rmw_bytes other than those four, or an
+ * lds_bytes outside 0 .. 65536; LORA_EHIP when the launch fails.  n_groups == 0 launches
  * nothing.  Asynchronous on `stream`. */
 lora_status lora_calib_gather_read(const void *pool, const int64_t *off, int32_t n_groups, int32_t blocks_per_group,
-                                   int32_t block_bytes, void *rmw, int32_t rmw_bytes, uint32_t *sink,
-                                   hipStream_t stream);
+                                   int32_t block_bytes, void *rmw, int32_t rmw_bytes, int32_t lds_bytes,
+                                   uint32_t *sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -84,7 +84,7 @@ def lib() -> ctypes.CDLL:
             "lora_merge": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, P, I64, P]),
             "lora_merge_multi": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, I32, P, I32, P]),
             "lora_pool_load": (ctypes.c_int, [pp, I32, P, P, P]),
-            "lora_calib_gather_read": (ctypes.c_int, [P, P, I32, I32, I32, P, I32, P, P]),
+            "lora_calib_gather_read": (ctypes.c_int, [P, P, I32, I32, I32, P, I32, I32, P, P]),
             "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "lora_abi_version": (I32, []),
         }
@@ -381,13 +381,16 @@ def plan_header(plan):
     return plan[:256].view(_torch().int32).cpu().tolist()[:16]
 
 
-def lora_calib_gather_read(pool, off, blocks_per_group: int, block_bytes: int, sink, rmw=None, rmw_bytes: int = 0):
+def lora_calib_gather_read(pool, off, blocks_per_group: int, block_bytes: int, sink, rmw=None, rmw_bytes: int = 0,
+                           lds_bytes: int = 0):
     """Measurement aid (include/lora_calib.h): workgroup g reads the
     blocks_per_group blocks of `pool` (a device tensor) that start at byte
     offsets off[g * blocks_per_group ...] (int64 device tensor), block_bytes
     each; with `rmw` it also reads and writes back rmw_bytes of rmw at
-    g * rmw_bytes.  sink (int32 device tensor, one word per group) receives
-    each group's XOR.  The caller keeps every block inside `pool`."""
+    g * rmw_bytes.  Each workgroup reserves lds_bytes of LDS it does not use
+    (limiting how many share a compute unit).  sink (int32 device tensor, one
+    word per group) receives each group's XOR.  The caller keeps every block
+    inside `pool`."""
     torch = _torch()
     if off.dtype != torch.int64 or blocks_per_group < 1 or off.numel() % blocks_per_group:
         raise LoraError(-2, "lora_calib_gather_read: off must be int64, blocks_per_group offsets per group")
@@ -398,5 +401,5 @@ def lora_calib_gather_read(pool, off, blocks_per_group: int, block_bytes: int, s
         raise LoraError(-2, "lora_calib_gather_read: rmw must hold rmw_bytes per group")
     _same_device("lora_calib_gather_read", pool.device, off, sink, rmw)
     _check(lib().lora_calib_gather_read(_ptr(pool), _ptr(off), n_groups, blocks_per_group, block_bytes, _ptr(rmw),
-                                        rmw_bytes if rmw is not None else 0, _ptr(sink), _stream(pool)),
+                                        rmw_bytes if rmw is not None else 0, lds_bytes, _ptr(sink), _stream(pool)),
            "lora_calib_gather_read")

@@ -71,14 +71,19 @@ __global__ __launch_bounds__(kCalibThreads) void gather_read_kernel(const unsign
 
 extern "C" lora_status lora_calib_gather_read(const void *pool, const int64_t *off, int32_t n_groups,
                                               int32_t blocks_per_group, int32_t block_bytes, void *rmw,
-                                              int32_t rmw_bytes, uint32_t *sink, hipStream_t stream) {
+                                              int32_t rmw_bytes, int32_t lds_bytes, uint32_t *sink,
+                                              hipStream_t stream) {
   if (!pool || !off || !sink || n_groups < 0) return LORA_EINVAL;
   if (blocks_per_group < 1 || block_bytes <= 0 || block_bytes % lora::kCalibRound != 0) return LORA_ESHAPE;
   if (rmw && (rmw_bytes <= 0 || rmw_bytes % lora::kCalibRmwPiece != 0 ||
               rmw_bytes > lora::kCalibRmwMax * lora::kCalibRmwPiece))
     return LORA_ESHAPE;
+  if (lds_bytes < 0 || lds_bytes > 65536) return LORA_ESHAPE;
   if (n_groups == 0) return LORA_OK;
-  hipLaunchKernelGGL(lora::gather_read_kernel, dim3(n_groups), dim3(lora::kCalibThreads), 0, stream,
+  static const bool lds_limit_raised =
+      lora::raise_lds_limit(reinterpret_cast<const void *>(&lora::gather_read_kernel), lora::kMaxLdsBytes);
+  (void)lds_limit_raised;
+  hipLaunchKernelGGL(lora::gather_read_kernel, dim3(n_groups), dim3(lora::kCalibThreads), size_t(lds_bytes), stream,
                      static_cast<const unsigned char *>(pool), off, blocks_per_group, block_bytes,
                      static_cast<unsigned char *>(rmw), rmw ? rmw_bytes : 0, sink);
   return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;

@@ -211,14 +211,15 @@ def test_sliced_table_layout_and_checks():
 
 def test_calib_gather_read_host_checks(lib):
     f = lib.lora_calib_gather_read
-    ok = dict(pool=FAKE, off=FAKE, n=4, bpg=2, bb=1 << 17, rmw=None, rb=0, sink=FAKE * 2)
+    ok = dict(pool=FAKE, off=FAKE, n=4, bpg=2, bb=1 << 17, rmw=None, rb=0, lds=0, sink=FAKE * 2)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["pool"], a["off"], a["n"], a["bpg"], a["bb"], a["rmw"], a["rb"], a["sink"], None)
+        return f(a["pool"], a["off"], a["n"], a["bpg"], a["bb"], a["rmw"], a["rb"], a["lds"], a["sink"], None)
 
     assert call(pool=None) == -1 and call(off=None) == -1 and call(sink=None) == -1 and call(n=-1) == -1
     assert call(bpg=0) == -2 and call(bb=0) == -2 and call(bb=16384) == -2
     assert call(rmw=FAKE * 3, rb=0) == -2 and call(rmw=FAKE * 3, rb=1000) == -2
     assert call(rmw=FAKE * 3, rb=5 * 4096) == -2
-    assert call(n=0) == 0 and call(n=0, rmw=FAKE * 3, rb=8192) == 0  # nothing to read: nothing launched
+    assert call(lds=-1) == -2 and call(lds=65537) == -2
+    assert call(n=0) == 0 and call(n=0, rmw=FAKE * 3, rb=8192, lds=65536) == 0  # nothing to read: nothing launched

@@ -13,8 +13,9 @@ from _gpu import DEV
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("blk,bpg,rmw_bytes", [(32768, 1, 0), (131072, 1, 0), (131072, 2, 8192), (65536, 3, 16384)])
-def test_gather_read_xor(blk, bpg, rmw_bytes):
+@pytest.mark.parametrize("blk,bpg,rmw_bytes,lds", [(32768, 1, 0, 0), (131072, 1, 0, 65536), (131072, 2, 8192, 65536),
+                                                   (65536, 3, 16384, 0)])
+def test_gather_read_xor(blk, bpg, rmw_bytes, lds):
     rng = np.random.default_rng(11)
     n_slots, n_groups = 24, 7
     host = rng.integers(0, 2**32, size=(n_slots * blk) // 4, dtype=np.uint32)
@@ -26,7 +27,7 @@ def test_gather_read_xor(blk, bpg, rmw_bytes):
     if rmw_bytes:
         rmw_host = rng.integers(0, 2**32, size=n_groups * rmw_bytes // 4, dtype=np.uint32)
         rmw = torch.from_numpy(rmw_host.view(np.int32)).to(DEV)
-    L.lora_calib_gather_read(pool, off, bpg, blk, sink, rmw=rmw, rmw_bytes=rmw_bytes)
+    L.lora_calib_gather_read(pool, off, bpg, blk, sink, rmw=rmw, rmw_bytes=rmw_bytes, lds_bytes=lds)
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
     words = host.reshape(n_slots, blk // 4)[pick].reshape(n_groups, -1)
