@@ -63,11 +63,18 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
   for (int kk = 0; kk < nact; ++kk) {
     const T *Aa = static_cast<const T *>(pr.A) + (int64_t)uniform(M.a[kk]) * r * d_in;
     const int rk = uniform(M.rk[kk]);  // the adapter's rank: rows past it are not read, their sums are 0
-    for (int j0 = w * kJPW; j0 < r; j0 += (kValuThreads / 64) * kJPW) {
+    constexpr int kPass = (kValuThreads / 64) * kJPW;  // rank rows of a pass over the four waves
+    for (int p0 = 0; p0 < r; p0 += kPass) {
+      // this wave's rows of the pass: jb + js * i.  When the adapter's rank
+      // covers the whole pass they are interleaved over the waves (rows w,
+      // w + 4, w + 8, w + 12), which reads A faster than four consecutive rows
+      // per wave; otherwise consecutive, so that waves past the rank skip it.
+      const bool il = p0 + kPass <= rk;
+      const int jb = il ? p0 + w : p0 + w * kJPW, js = il ? kValuThreads / 64 : 1;
       float acc[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-      for (int c0 = lane; c0 < (j0 < rk ? nvx : 0); c0 += 64 * UB) {
+      for (int c0 = lane; c0 < (jb < rk ? nvx : 0); c0 += 64 * UB) {
         V xv[UB][MB], av[UB][kJPW];
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
@@ -76,7 +83,7 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
 #pragma unroll
           for (int m = 0; m < MB; ++m) xv[u][m] = gload_at<V>(xrow[m], off);
 #pragma unroll
-          for (int i = 0; i < kJPW; ++i) av[u][i] = gload_at<V>(Aa, uint32_t(min(j0 + i, rk - 1)) * row_bytes + off);
+          for (int i = 0; i < kJPW; ++i) av[u][i] = gload_at<V>(Aa, uint32_t(min(jb + js * i, rk - 1)) * row_bytes + off);
           if (cv >= nvx) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) xv[u][m] = O::zero();
@@ -97,7 +104,7 @@ __device__ void valu_shrink(const ApplyArgs &a, const lora_problem &pr, int m0, 
 #pragma unroll
         for (int i = 0; i < kJPW; ++i) part[i] = acc[m * kJPW + i];
         const float val = wave_sum_scatter<kJPW>(part);
-        const int j = j0 + lane;
+        const int j = jb + js * lane;
         if (lane < kJPW && m < nb && j < r) {
           const float vs = j < rk ? val * M.sc[m0 + m][kk] : 0.f;
           if constexpr (MODE == MODE_SHRINK)
