@@ -184,7 +184,14 @@ Launch configure(int mode, const lora_pool *shape, const BatchDims &d, const Pla
   const int64_t items_m = (int64_t)n_groups * std::max(P.L.bound_m, P.L.bound_ms) * a.cmo[ns];
   // the VALU kernel takes an MFMA-sized tile as one item per row block
   const int64_t items_mv = (int64_t)n_groups * P.L.bound_m * a.cmo[ns] * (kMfmaRows / kRowBlock);
-  const int64_t items_v = (int64_t)n_groups * ((int64_t)P.L.bound_v * a.cvo[ns]) + (a.valu_takes_m ? items_mv : 0);
+  // VALU tiles come only from adapter groups of fewer than kMfmaMinRows rows
+  // (at most four tiles each), and a batch has at most one group per request
+  // (per adapter too with one slot per request): a batch of long requests
+  // gets a small VALU grid instead of one sized by its rows
+  const int64_t groups_max = d.K == 1 ? std::min(d.S, shape->n_adapters) : d.S;
+  const int64_t tiles_v =
+      std::min<int64_t>(P.L.bound_v, (kMfmaMinRows - 2 + kValuRows) / kValuRows * std::max<int64_t>(groups_max, 1));
+  const int64_t items_v = (int64_t)n_groups * (tiles_v * a.cvo[ns]) + (a.valu_takes_m ? items_mv : 0);
   L.grid_v = round_up((int)std::max<int64_t>(std::min<int64_t>(items_v, tn.grid_cap), 1), 8);
   L.grid_m = mfma ? round_up((int)std::max<int64_t>(std::min<int64_t>(items_m, tn.grid_cap), 1), 8) : 0;
   L.smem_v = valu_smem_bytes(a.kr_max);
