@@ -223,3 +223,21 @@ def test_calib_gather_read_host_checks(lib):
     assert call(rmw=FAKE * 3, rb=5 * 4096) == -2
     assert call(lds=-1) == -2 and call(lds=65537) == -2
     assert call(n=0) == 0 and call(n=0, rmw=FAKE * 3, rb=8192, lds=65536) == 0  # nothing to read: nothing launched
+
+
+def test_calib_binding_checks():
+    """The binding refuses offsets that are not int64, an offset count that is
+    not whole groups, and a sink or slice buffer too small, before any pointer
+    reaches the library (CPU tensors: nothing is launched)."""
+    import torch
+    pool = torch.zeros(1 << 16, dtype=torch.uint8)
+    sink = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(L.LoraError):
+        L.lora_calib_gather_read(pool, torch.zeros(4, dtype=torch.int32), 1, 32768, sink)
+    with pytest.raises(L.LoraError):
+        L.lora_calib_gather_read(pool, torch.zeros(5, dtype=torch.int64), 2, 32768, sink)
+    with pytest.raises(L.LoraError):
+        L.lora_calib_gather_read(pool, torch.zeros(8, dtype=torch.int64), 1, 32768, sink)
+    with pytest.raises(L.LoraError):
+        L.lora_calib_gather_read(pool, torch.zeros(4, dtype=torch.int64), 1, 32768, sink,
+                                 rmw=torch.zeros(4096, dtype=torch.uint8), rmw_bytes=4096)
