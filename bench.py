@@ -583,6 +583,21 @@ def calibration(dev, reps=20):
                                                       lds_bytes=65536), True)
     del pool, rmw
     pair_bytes = n_blk * blk + 2 * (n_blk // 2) * 8192
+    # The 4096-wide rank-64 prefill batch of 32 requests over 8 adapters
+    # (16997 rows in 392 tiles of up to 48) as 392 full 48-row tiles, with no
+    # arithmetic (lora_calib_tile_stream): x read and y read and written back
+    # in the MFMA kernel's stage order with the tile's A and B beside each
+    # stage, the same without A and B, and whole rows at a time.
+    n_tiles, t_rows, t_rb = 392, 48, 8192
+    tx = torch.zeros(n_tiles * t_rows * t_rb, dtype=torch.uint8, device=dev)
+    ty = torch.zeros_like(tx)
+    tad = torch.zeros(8 * (t_rb // 512 * 32768 + t_rb // 256 * 16384), dtype=torch.uint8, device=dev)
+    tsink = torch.empty(n_tiles, dtype=torch.int32, device=dev)
+    tiles_ms = {k: timed(lambda o=o, a=a: L.lora_calib_tile_stream(tx, ty, t_rows, t_rb, tsink, order=o, adapters=a,
+                                                                   n_adapters=8 if a is not None else 0), True)
+                for k, o, a in (("stage_order_with_A_B", 0, tad), ("stage_order", 0, None), ("row_order", 1, None))}
+    del tx, ty, tad
+    tile_bytes = 3 * n_tiles * t_rows * t_rb
     return {"copy_1GiB_GBps": 2 * n / (copy_ms * 1e-3) / 1e9, "read_1GiB_GBps": n / (read_ms * 1e-3) / 1e9,
             "gather_read": {"what": f"{n_blk} blocks of 128 KB at random places of a 4 GiB pool, one workgroup each",
                             "bytes": n_blk * blk, "us": round(one_ms * 1e3, 3),
@@ -594,6 +609,13 @@ def calibration(dev, reps=20):
                                 "GBps": pair_bytes / (pair_ms * 1e-3) / 1e9,
                                 "two_per_cu_us": round(pair2_ms * 1e3, 3),
                                 "two_per_cu_GBps": pair_bytes / (pair2_ms * 1e-3) / 1e9},
+            "prefill_tile_skeleton": {"what": f"{n_tiles} tiles of {t_rows} rows of x (read) and y (read and "
+                                              f"written back), {t_rb} bytes a row, no arithmetic; "
+                                              "stage_order_with_A_B also reads its tile's adapter's A and B "
+                                              "(1 MB, 8 adapters) a stage at a time",
+                                      "bytes": tile_bytes,
+                                      **{f"{k}_us": round(v * 1e3, 3) for k, v in tiles_ms.items()},
+                                      **{f"{k}_GBps": tile_bytes / (v * 1e-3) / 1e9 for k, v in tiles_ms.items()}},
             "empty_kernel_floor_us": round(floor_ms * 1e3, 3),
             "note": "torch copy_ and sum, and the library's gather-read probe, each after a cache flush; medians "
                     "of HIP-event times"}

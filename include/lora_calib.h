@@ -52,6 +52,35 @@ lora_status lora_calib_gather_read(const void *pool, const int64_t *off, int32_t
                                    int32_t block_bytes, void *rmw, int32_t rmw_bytes, int32_t lds_bytes,
                                    uint32_t *sink, hipStream_t stream);
 
+/* The traffic of the MFMA kernel's prefill tiles with none of their
+ * arithmetic.  Workgroup t owns rows t*rows .. t*rows + rows - 1 of x and of y
+ * (row stride row_bytes; 8192 for a 4096-wide bf16 layer).
+ *   order 0, the MFMA kernel's stages: row_bytes / 512 shrink stages, each
+ *     reading 512 bytes of every row of x and, with adapters, 32 KB of the
+ *     tile's A; then row_bytes / 256 expand stages, each reading 256 bytes of
+ *     every row of y and, with adapters, 16 KB of B, and writing those bytes
+ *     of y back; a workgroup barrier in every stage.  Tile t reads adapter
+ *     t % n_adapters: A of row_bytes / 512 * 32 KB bytes followed by B of
+ *     row_bytes / 256 * 16 KB bytes (a rank-64 adapter of the layer: 512 KB
+ *     each at row_bytes 8192).
+ *   order 1, whole rows: each wave reads its rows of x one after another, 1 KB
+ *     per load instruction, then reads and writes back its rows of y the same
+ *     way; adapters are not read.
+ * The values of y are unchanged.  sink[t] = the XOR of every 32-bit word the
+ * tile read (x, y and adapter bytes).  lds_bytes as for lora_calib_gather_read.
+ *   x, y       device, n_tiles * rows * row_bytes bytes each
+ *   adapters   device, n_adapters * (row_bytes / 512 * 32768 + row_bytes / 256 * 16384)
+ *              bytes, or NULL
+ *   sink       device, n_tiles words, written
+ * Returns LORA_EINVAL for NULL x, y or sink, n_tiles < 0, or adapters with
+ * n_adapters < 1; LORA_ESHAPE for rows outside 1 .. 64, a row_bytes that is not
+ * a multiple of 1024 in 1024 .. 65536, an order other than 0 or 1, or an
+ * lds_bytes outside 0 .. 65536; LORA_EHIP when the launch fails.  n_tiles == 0
+ * launches nothing.  Asynchronous on `stream`. */
+lora_status lora_calib_tile_stream(const void *x, void *y, int32_t n_tiles, int32_t rows, int32_t row_bytes,
+                                   const void *adapters, int32_t n_adapters, int32_t order, int32_t lds_bytes,
+                                   uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,8 @@ Functions carry the C names:
   lora_workspace_size, lora_plan_build, lora_apply, lora_apply_noalloc, lora_shrink, lora_expand,
   lora_apply_planned, lora_shrink_planned, lora_expand_planned,
   lora_apply_multi, lora_apply_sliced, lora_read_device_errors, lora_status_string,
-  and the measurement aid lora_calib_gather_read (include/lora_calib.h).
+  and the measurement aids lora_calib_gather_read and lora_calib_tile_stream
+  (include/lora_calib.h).
 
 Tensors: A [n][r][d_in] and B [n][d_out][r] contiguous (float32 or bfloat16);
 x [T][ldx], y [T][ldy] with unit column stride (ld = stride(0)); idx int32
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "lora_merge_multi": (ctypes.c_int, [pp, P, P, I32, ctypes.c_float, I32, P, I32, P]),
             "lora_pool_load": (ctypes.c_int, [pp, I32, P, P, P]),
             "lora_calib_gather_read": (ctypes.c_int, [P, P, I32, I32, I32, P, I32, I32, P, P]),
+            "lora_calib_tile_stream": (ctypes.c_int, [P, P, I32, I32, I32, P, I32, I32, I32, P, P]),
             "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "lora_abi_version": (I32, []),
         }
@@ -403,3 +405,29 @@ def lora_calib_gather_read(pool, off, blocks_per_group: int, block_bytes: int, s
     _check(lib().lora_calib_gather_read(_ptr(pool), _ptr(off), n_groups, blocks_per_group, block_bytes, _ptr(rmw),
                                         rmw_bytes if rmw is not None else 0, lds_bytes, _ptr(sink), _stream(pool)),
            "lora_calib_gather_read")
+
+
+def lora_calib_tile_stream(x, y, rows: int, row_bytes: int, sink, order: int = 0, adapters=None,
+                           n_adapters: int = 0, lds_bytes: int = 0):
+    """Measurement aid (include/lora_calib.h): the prefill tiles' traffic with
+    no arithmetic.  Workgroup t reads its `rows` rows (row_bytes each) of the
+    device tensors x and y and writes y's back unchanged, in the MFMA
+    kernel's stage order (order 0, reading a stage of adapter t % n_adapters
+    beside each when `adapters` is given) or whole rows at a time (order 1).
+    sink (int32 device tensor, one word per tile) receives each tile's XOR."""
+    if rows < 1 or row_bytes < 1 or x.numel() * x.element_size() % (rows * row_bytes):
+        raise LoraError(-2, "lora_calib_tile_stream: x must hold whole tiles of rows x row_bytes")
+    n_tiles = x.numel() * x.element_size() // (rows * row_bytes)
+    if y.numel() * y.element_size() != x.numel() * x.element_size():
+        raise LoraError(-2, "lora_calib_tile_stream: y must be the size of x")
+    if sink.numel() * sink.element_size() < 4 * n_tiles:
+        raise LoraError(-2, "lora_calib_tile_stream: sink must hold one word per tile")
+    if adapters is not None:
+        per = row_bytes // 512 * 32768 + row_bytes // 256 * 16384
+        if n_adapters < 1 or adapters.numel() * adapters.element_size() < n_adapters * per:
+            raise LoraError(-2, "lora_calib_tile_stream: adapters must hold n_adapters A and B blocks")
+    _same_device("lora_calib_tile_stream", x.device, y, sink, adapters)
+    _check(lib().lora_calib_tile_stream(_ptr(x), _ptr(y), n_tiles, rows, row_bytes, _ptr(adapters),
+                                        n_adapters if adapters is not None else 0, order, lds_bytes, _ptr(sink),
+                                        _stream(x)),
+           "lora_calib_tile_stream")

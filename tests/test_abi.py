@@ -225,6 +225,22 @@ def test_calib_gather_read_host_checks(lib):
     assert call(n=0) == 0 and call(n=0, rmw=FAKE * 3, rb=8192, lds=65536) == 0  # nothing to read: nothing launched
 
 
+def test_calib_tile_stream_host_checks(lib):
+    f = lib.lora_calib_tile_stream
+    ok = dict(x=FAKE, y=FAKE * 2, n=4, rows=48, rb=8192, ad=None, na=0, order=0, lds=0, sink=FAKE * 3)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["y"], a["n"], a["rows"], a["rb"], a["ad"], a["na"], a["order"], a["lds"], a["sink"], None)
+
+    assert call(x=None) == -1 and call(y=None) == -1 and call(sink=None) == -1 and call(n=-1) == -1
+    assert call(ad=FAKE * 4, na=0) == -1
+    assert call(rows=0) == -2 and call(rows=65) == -2 and call(rb=512) == -2 and call(rb=1536) == -2
+    assert call(rb=65536 + 1024) == -2 and call(order=2) == -2 and call(order=-1) == -2
+    assert call(lds=-1) == -2 and call(lds=65537) == -2
+    assert call(n=0) == 0 and call(n=0, ad=FAKE * 4, na=8, order=1, lds=65536) == 0  # nothing launched
+
+
 def test_calib_binding_checks():
     """The binding refuses offsets that are not int64, an offset count that is
     not whole groups, and a sink or slice buffer too small, before any pointer
@@ -241,3 +257,13 @@ def test_calib_binding_checks():
     with pytest.raises(L.LoraError):
         L.lora_calib_gather_read(pool, torch.zeros(4, dtype=torch.int64), 1, 32768, sink,
                                  rmw=torch.zeros(4096, dtype=torch.uint8), rmw_bytes=4096)
+    x = torch.zeros(4 * 2 * 1024, dtype=torch.uint8)  # four tiles of 2 rows of 1 KB
+    with pytest.raises(L.LoraError):  # not whole tiles
+        L.lora_calib_tile_stream(x, x.clone(), 3, 1024, sink)
+    with pytest.raises(L.LoraError):  # y not the size of x
+        L.lora_calib_tile_stream(x, x[:1024].clone(), 2, 1024, sink)
+    with pytest.raises(L.LoraError):  # sink too small
+        L.lora_calib_tile_stream(x, x.clone(), 2, 1024, sink[:3])
+    with pytest.raises(L.LoraError):  # adapters too small for n_adapters
+        L.lora_calib_tile_stream(x, x.clone(), 2, 1024, sink, adapters=torch.zeros(1 << 16, dtype=torch.uint8),
+                                 n_adapters=2)

@@ -1,4 +1,4 @@
-"""The gather-read probe (include/lora_calib.h), a measurement aid the
+"""The gather-read and tile-stream probes (include/lora_calib.h), measurement aids the
 benchmark reports beside the LoRA kernels: every block a group is given is
 read whole, so each sink word equals the XOR of that group's 32-bit words
 (computed here with numpy, exactly); the read-and-write-back slice keeps its
@@ -34,3 +34,34 @@ def test_gather_read_xor(blk, bpg, rmw_bytes, lds):
     assert np.array_equal(got, np.bitwise_xor.reduce(words, axis=1))
     if rmw is not None:
         assert np.array_equal(rmw.cpu().numpy().view(np.uint32), rmw_host)
+
+
+@pytest.mark.parametrize("rows,row_bytes,order,n_ad,lds", [(48, 8192, 0, 3, 0), (48, 8192, 1, 0, 65536),
+                                                          (5, 2048, 0, 0, 0), (64, 3072, 1, 0, 0),
+                                                          (17, 1024, 0, 2, 65536)])
+def test_tile_stream_xor(rows, row_bytes, order, n_ad, lds):
+    """The tile-stream probe reads every byte of its tiles of x and y (and, in
+    stage order, of its adapter's A and B) exactly once and writes y back
+    unchanged: each sink word is that XOR, computed here with numpy."""
+    rng = np.random.default_rng(12)
+    n_tiles = 7
+    words = n_tiles * rows * row_bytes // 4
+    xh = rng.integers(0, 2**32, size=words, dtype=np.uint32)
+    yh = rng.integers(0, 2**32, size=words, dtype=np.uint32)
+    x = torch.from_numpy(xh.view(np.int32)).to(DEV)
+    y = torch.from_numpy(yh.view(np.int32)).to(DEV)
+    sink = torch.zeros(n_tiles, dtype=torch.int32, device=DEV)
+    ad = adh = None
+    per = row_bytes // 512 * 32768 + row_bytes // 256 * 16384
+    if n_ad:
+        adh = rng.integers(0, 2**32, size=n_ad * per // 4, dtype=np.uint32)
+        ad = torch.from_numpy(adh.view(np.int32)).to(DEV)
+    L.lora_calib_tile_stream(x, y, rows, row_bytes, sink, order=order, adapters=ad, n_adapters=n_ad, lds_bytes=lds)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(xh.reshape(n_tiles, -1), axis=1) ^ np.bitwise_xor.reduce(yh.reshape(n_tiles, -1),
+                                                                                            axis=1)
+    if n_ad and order == 0:
+        ad_xor = np.bitwise_xor.reduce(adh.reshape(n_ad, -1), axis=1)
+        want = want ^ ad_xor[np.arange(n_tiles) % n_ad]
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), yh)
