@@ -569,7 +569,6 @@ lora_status merge_slots(const lora_pool *shape, const int32_t *idx, const float 
   a.ranks = shape->ranks;
   a.d_in = shape->d_in;
   a.d_out = shape->d_out;
-  a.n_strips = (shape->d_in + 127) / 128;
   return LORA_OK;
 }
 

@@ -193,7 +193,6 @@ struct MergeArgs {
   int nslots;  // active slots, 1 .. LORA_MAX_SLOTS
   int r, d_in, d_out;
   const int *ranks;  // per-adapter ranks (device), or nullptr
-  int n_strips;  // column strips of the matrix-core path
   int aligned;   // every problem's pointers and ldw allow 16-byte accesses
 };
 bool merge_mfma_eligible(const MergeArgs &a, int dtype);

@@ -9,7 +9,7 @@
 // bandwidth).
 //
 // bf16: the update is a dense contraction of rank K*r, so it runs on the
-// matrix cores.  A workgroup owns a strip of kStripCols columns of W and walks
+// matrix cores.  A workgroup owns a strip of 128 or 256 columns of W and walks
 // down it in steps of 64 rows (16 per wave).  A^T of the strip (every slot,
 // rank padded to a multiple of 32 with zeros) is staged once in LDS, with the
 // columns of each 32-column group interleaved so that the accumulators of two
@@ -30,7 +30,14 @@
 namespace lora {
 namespace {
 
-constexpr int kStripCols = 128;  // columns of W per strip (MFMA path)
+// Columns of W per strip (MFMA path): 256 where the build keeps its ring in
+// registers without spilling (one slot up to rank 64, or rank 128 alone), 128
+// otherwise.  Each row of a step then moves 512 bytes in and out rather than
+// 256: the FLUX-sized rank-64 merge ran 2085 -> 1929 us.
+template <int KSR, int NE>
+constexpr int strip_cols() {
+  return (NE <= 2 || (KSR == 4 && NE == 4)) ? 256 : 128;
+}
 constexpr int kStepRows = 64;    // rows per step: 16 per wave
 constexpr int kStepsPerItem = 16;  // 1024 rows per item: 8 measured 1.2% slower, 24 and 48 2-4% slower (balance)
 
@@ -62,13 +69,14 @@ __device__ __forceinline__ int strip_row(int c) {
 template <int KSR, int NE>
 __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kStripCols = strip_cols<KSR, NE>();
   uint16_t *at = reinterpret_cast<uint16_t *>(smem);  // [slot][kStripCols][RP + 8]
   constexpr int RP = 32 * KSR, AST = RP + 8;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
   const int r = a.r, d_in = a.d_in, d_out = a.d_out, ns = a.nslots;
   const int n_chunks = (d_out + kStepRows * kStepsPerItem - 1) / (kStepRows * kStepsPerItem);
-  const int64_t per_prob = (int64_t)a.n_strips * n_chunks;
+  const int64_t per_prob = (int64_t)((d_in + kStripCols - 1) / kStripCols) * n_chunks;
 
   walk_items(per_prob * a.n_problems, 1, [&](int64_t item) {
     const int p = int(item / per_prob);
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void merge_mfma_kernel(MergeArgs a) {
     //     slots are fixed at compile time (no copies: copying a register whose
     //     load is in flight would wait for it).  Steps past the end re-read the
     //     last one (never used), so that every path issues the same loads.
-    constexpr int NP = kStripCols / 32, D = NE >= 8 ? 2 : 3;
+    constexpr int NP = kStripCols / 32, D = (NE >= 8 || NP > 4) ? 2 : 3;
     uint4 wr[D][NP], br[D][NE];
     const int n_steps = min(kStepsPerItem, (d_out - row0 + kStepRows - 1) / kStepRows);
     auto load = [&](int step, uint4(&wv)[NP], uint4(&bv)[NE]) {
@@ -250,7 +258,12 @@ __global__ __launch_bounds__(kThreads) void merge_valu_kernel(MergeArgs a) {
 }
 
 template <int KSR, int NE>
-hipError_t launch_mfma_ksr(const MergeArgs &a, int grid, size_t smem, hipStream_t stream) {
+hipError_t launch_mfma_ksr(const MergeArgs &a, hipStream_t stream) {
+  constexpr int kStripCols = strip_cols<KSR, NE>();
+  const int n_chunks = (a.d_out + kStepRows * kStepsPerItem - 1) / (kStepRows * kStepsPerItem);
+  const int64_t items = (int64_t)((a.d_in + kStripCols - 1) / kStripCols) * n_chunks * a.n_problems;
+  const int grid = int(std::min<int64_t>((items + 7) / 8 * 8, 2048));
+  const size_t smem = size_t(a.nslots) * kStripCols * (32 * KSR + 8) * 2;
   static const bool lds_limit_raised =
       raise_lds_limit(reinterpret_cast<const void *>(&merge_mfma_kernel<KSR, NE>), kMaxLdsBytes);
   (void)lds_limit_raised;
@@ -260,12 +273,12 @@ hipError_t launch_mfma_ksr(const MergeArgs &a, int grid, size_t smem, hipStream_
 
 // NE: the (slot, k-step) entries, rounded up to 1, 2, 4 or 8.
 template <int KSR>
-hipError_t launch_mfma_ne(const MergeArgs &a, int grid, size_t smem, hipStream_t stream) {
+hipError_t launch_mfma_ne(const MergeArgs &a, hipStream_t stream) {
   const int ne = a.nslots * KSR;
-  if (ne <= 1 && KSR <= 1) return launch_mfma_ksr<KSR, (KSR <= 1 ? 1 : KSR)>(a, grid, smem, stream);
-  if (ne <= 2 && KSR <= 2) return launch_mfma_ksr<KSR, (KSR <= 2 ? 2 : KSR)>(a, grid, smem, stream);
-  if (ne <= 4 && KSR <= 4) return launch_mfma_ksr<KSR, (KSR <= 4 ? 4 : KSR)>(a, grid, smem, stream);
-  return launch_mfma_ksr<KSR, 8>(a, grid, smem, stream);
+  if (ne <= 1 && KSR <= 1) return launch_mfma_ksr<KSR, (KSR <= 1 ? 1 : KSR)>(a, stream);
+  if (ne <= 2 && KSR <= 2) return launch_mfma_ksr<KSR, (KSR <= 2 ? 2 : KSR)>(a, stream);
+  if (ne <= 4 && KSR <= 4) return launch_mfma_ksr<KSR, (KSR <= 4 ? 4 : KSR)>(a, stream);
+  return launch_mfma_ksr<KSR, 8>(a, stream);
 }
 
 }  // namespace
@@ -279,15 +292,11 @@ hipError_t launch_merge(const MergeArgs &a, int dtype, hipStream_t stream) {
   if (merge_mfma_eligible(a, dtype)) {
     const int ksr = (a.r + 31) / 32;
     const int k2 = ksr <= 1 ? 1 : ksr <= 2 ? 2 : ksr <= 4 ? 4 : 8;
-    const int n_chunks = (a.d_out + kStepRows * kStepsPerItem - 1) / (kStepRows * kStepsPerItem);
-    const int64_t items = (int64_t)a.n_strips * n_chunks * a.n_problems;
-    const int grid = int(std::min<int64_t>((items + 7) / 8 * 8, 2048));
-    const size_t smem = size_t(a.nslots) * kStripCols * (32 * k2 + 8) * 2;
     switch (k2) {
-      case 1: return launch_mfma_ne<1>(a, grid, smem, stream);
-      case 2: return launch_mfma_ne<2>(a, grid, smem, stream);
-      case 4: return launch_mfma_ne<4>(a, grid, smem, stream);
-      default: return launch_mfma_ne<8>(a, grid, smem, stream);
+      case 1: return launch_mfma_ne<1>(a, stream);
+      case 2: return launch_mfma_ne<2>(a, stream);
+      case 4: return launch_mfma_ne<4>(a, stream);
+      default: return launch_mfma_ne<8>(a, stream);
     }
   }
   const int64_t items = (int64_t)((a.d_in + kValuCols - 1) / kValuCols) *

@@ -61,6 +61,9 @@ GRID = {
     "bf16_r256_k1": dict(dtype=W.BF16, n=2, r=256, d_in=384, d_out=70, K=1),
     "bf16_r8_k8_empty": dict(dtype=W.BF16, n=9, r=8, d_in=128, d_out=64, K=8, p_empty=0.3),
     "bf16_ldw_padded": dict(dtype=W.BF16, n=3, r=32, d_in=256, d_out=300, K=1, ldw=272),
+    # 256-column strips (one slot up to rank 64, rank 128 alone): a ragged last strip, rows past one item
+    "bf16_r64_k1_wide_ragged": dict(dtype=W.BF16, n=3, r=64, d_in=776, d_out=1100, K=1),
+    "bf16_r128_k1_wide_ragged": dict(dtype=W.BF16, n=2, r=128, d_in=392, d_out=100, K=1, alpha=-1.0),
     # VALU path: fp32, odd shapes, K * r beyond the matrix-core limit
     "f32_r64_k2": dict(dtype=W.F32, n=4, r=64, d_in=200, d_out=150, K=2),
     "f32_r5_odd": dict(dtype=W.F32, n=3, r=5, d_in=37, d_out=23, K=2, ldw=41, alpha=-1.0),
