@@ -262,7 +262,9 @@ hipError_t launch_mfma_ksr(const MergeArgs &a, hipStream_t stream) {
   constexpr int kStripCols = strip_cols<KSR, NE>();
   const int n_chunks = (a.d_out + kStepRows * kStepsPerItem - 1) / (kStepRows * kStepsPerItem);
   const int64_t items = (int64_t)((a.d_in + kStripCols - 1) / kStripCols) * n_chunks * a.n_problems;
-  const int grid = int(std::min<int64_t>((items + 7) / 8 * 8, 2048));
+  // one item per workgroup up to 65536 items: the FLUX-sized merge's 8208
+  // items ran 1.5% faster so than walked by 2048 workgroups
+  const int grid = int(std::min<int64_t>((items + 7) / 8 * 8, 65536));
   const size_t smem = size_t(a.nslots) * kStripCols * (32 * KSR + 8) * 2;
   static const bool lds_limit_raised =
       raise_lds_limit(reinterpret_cast<const void *>(&merge_mfma_kernel<KSR, NE>), kMaxLdsBytes);
