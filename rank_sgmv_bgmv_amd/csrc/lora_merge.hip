@@ -39,7 +39,7 @@ constexpr int strip_cols() {
   return (NE <= 2 || (KSR == 4 && NE == 4)) ? 256 : 128;
 }
 constexpr int kStepRows = 64;    // rows per step: 16 per wave
-constexpr int kStepsPerItem = 16;  // 1024 rows per item: 8 measured 1.2% slower, 24 and 48 2-4% slower (balance)
+constexpr int kStepsPerItem = 8;  // 512 rows per item, one item per workgroup: 4, 6, 16, 24 and 48 measured 3-8% slower
 
 // f(std::integral_constant<int, i>{}) for i = 0 .. N-1: ring slot indices
 // that are constant expressions, so the ring stays in registers.
